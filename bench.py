@@ -1,0 +1,287 @@
+"""Benchmark: one Ulysses rank's attention hot path on one MI355X.
+
+A step is one pass of the whole hot path for one attention layer on one rank
+of a P-way Ulysses job (all-to-all exchange excluded: there is one GPU):
+    pack Q, K, V of this rank's sequence slice (send buffers)
+    attention forward over the full sequence on this rank's heads
+    unpack O back to the rank's slice
+    pack dO, attention backward, unpack dQ, dK, dV
+Inputs are seeded synthetic tensors resident in HBM before the timed region.
+
+Printed (one JSON line): value = attention FLOPs (algorithmic: causal pairs,
+4 d h_q per pair forward, 10 d h_q backward) of one step / step time. The
+line also carries forward-only and forward+backward attention rates, the
+permute bandwidth of the composite pack (all P ranks' Q, K and V), the
+roofline of the dominant kernel (live HIP-event timing through the library's
+kernel trace) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn TFLOP/s fwd & fwd+bwd at S=120K (4Q/1KV heads, d=128); permute GB/s"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0       # HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="s120k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=12000)
+    return ap.parse_args()
+
+
+def causal_pairs(s: int) -> int:
+    return s * (s + 1) // 2
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "ulysses_sequence_parallelism_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# kernel -> (source files, algorithmic FLOP per causal pair per query head / d)
+KERNELS = {
+    "attn_fwd_bf16": (("attn_fwd_bf16.hip", "usp_common.h"), 4),
+    # the key-stationary kernel does 4 of the 5 backward products: QK^T, dO V^T,
+    # P^T dO, dS^T Q
+    "attn_bwd_dkdv_bf16": (("attn_bwd_bf16.hip", "usp_common.h"), 8),
+    # the query-stationary kernel does dS K (2d); its QK^T and dO V^T are
+    # recomputations beyond the algorithmic count
+    "attn_bwd_dq_bf16": (("attn_bwd_bf16.hip", "usp_common.h"), 2),
+}
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries
+    (profiles/traffic_<kernel>_<workload>.txt), or None when absent or taken
+    on a different version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path) or kernel not in KERNELS:
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != src_hash(*KERNELS[kernel][0]):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, rows: int):
+    """The fp64 oracle on the causal prefix [0, rows) of the rank's share:
+    rows < R only see keys < R, so this is exactly a bounded part of the
+    workload. Forward + full backward, all query heads."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    p, r = w.p, min(rows, w.s_pad)
+    share = []
+    for t in (workloads.Q, workloads.K, workloads.V, workloads.DO):
+        heads = w.hq_full if t in (workloads.Q, workloads.DO) else w.hkv_full
+        x = workloads.tensor(w, t, s=r)   # same draw prefix as the full tensor
+        share.append(x[:, : heads // p].to(torch.float64).numpy())
+    q, k, v, do = share
+    # the generator draws row-major, so the first r rows equal the full tensor's
+    t0 = time.perf_counter()
+    o, lse = oracle.attn_fwd(q, k, v, w.scale)
+    oracle.attn_bwd(q, k, v, o, lse, do, w.scale)
+    dt = time.perf_counter() - t0
+    flops = (4 + 10) * w.d * w.hq * causal_pairs(r)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"causal prefix rows 0..{r - 1} of the {w.name} rank share "
+                      f"({w.hq} Q / {w.hkv} KV heads, d={w.d}): fp64 forward + full backward, "
+                      f"{dt:.1f} s, {flops / 1e12:.3f} TFLOP algorithmic",
+            "seconds": dt, "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU's share only: the path runs on a single MI355X "
+              "(no collectives are built). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import ulysses_sequence_parallelism_amd as usp
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("no GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS[args.workload]
+    if w.dtype != "bf16" or w.thd:
+        print("bench workloads: s8k, s32k, s120k, s120k_pad", file=sys.stderr)
+        sys.exit(2)
+    p, s_pad, s_loc = w.p, w.s_pad, w.s_pad // w.p
+    hq, hkv, d = w.hq, w.hkv, w.d
+
+    # ---- inputs (seeded, resident in HBM before timing)
+    full = {}
+    for t in (workloads.Q, workloads.K, workloads.V, workloads.DO):
+        full[t] = workloads.tensor(w, t).to(dev)
+    # this rank's share: the composite pack's slice 0 (what the all-to-all delivers)
+    share = {t: usp.usp_pad_pack_seq2head(x, p)[0].contiguous() for t, x in full.items()}
+    q, k, v, do = (share[t] for t in (workloads.Q, workloads.K, workloads.V, workloads.DO))
+    # this rank's own sequence slice (all heads): what it packs into send buffers
+    local = {t: x[:s_loc].contiguous() for t, x in full.items()}
+    send = {t: torch.empty((p, s_loc, x.shape[1] // p, d), dtype=x.dtype, device=dev)
+            for t, x in local.items()}
+    o = torch.empty_like(q)
+    lse = torch.empty((hq, s_pad), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    back = {n: torch.empty((s_loc, p * a.shape[1], d), dtype=a.dtype, device=dev)
+            for n, a in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv))}
+    ws_f = torch.empty(max(1, usp.usp_attn_fwd_workspace_bytes(s_pad, hq, hkv, d, 0)),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(usp.usp_attn_bwd_workspace_bytes(s_pad, hq, hkv, d, 0),
+                       dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        for t in (workloads.Q, workloads.K, workloads.V):
+            usp.usp_pad_pack_seq2head(local[t], p, out=send[t])
+        usp.usp_attn_fwd(q, k, v, s_valid=w.s, out=o, lse=lse, workspace=ws_f)
+        usp.usp_unpack_head2seq(o.view(p, s_loc, hq, d), s_loc, out=back["o"])
+        usp.usp_pad_pack_seq2head(local[workloads.DO], p, out=send[workloads.DO])
+        usp.usp_attn_bwd(q, k, v, o, lse, do, s_valid=w.s, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+        for n, a in (("dq", dq), ("dk", dk), ("dv", dv)):
+            usp.usp_unpack_head2seq(a.view(p, s_loc, a.shape[1], d), s_loc, out=back[n])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, kernel trace on
+    usp.usp_trace_enable(True)
+    usp.usp_trace_collect()  # drop anything recorded before
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    usp.usp_trace_enable(False)
+    trace = usp.usp_trace_collect()
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+
+    pairs = causal_pairs(w.s_pad) if w.s == w.s_pad else causal_pairs(w.s) + (w.s_pad - w.s) * w.s
+    f_fwd = 4 * d * hq * pairs
+    f_bwd = 10 * d * hq * pairs
+    per = {e["name"]: e for e in trace}
+
+    def kms(*names):
+        return sum(per[n]["total_ms"] for n in names if n in per) / args.steps
+
+    fwd_ms = kms("attn_fwd_kmajor_v", "attn_fwd_bf16")
+    bwd_ms = kms("attn_bwd_kmajor", "attn_bwd_rowdot_bf16", "attn_bwd_dkdv_bf16", "attn_bwd_dq_bf16")
+    perm_ms = kms("pack_seq2head", "unpack_head2seq")
+
+    # ---- dominant kernel roofline
+    dom = max((e for e in trace if e["name"] in KERNELS), key=lambda e: e["total_ms"])
+    dom_avg_ms = dom["total_ms"] / dom["launches"]
+    dom_flops = KERNELS[dom["name"]][1] * d * hq * pairs
+    achieved = dom_flops / (dom_avg_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom["name"], "achieved": round(achieved, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_for(dom["name"], w.name),
+                "avg_launch_ms": round(dom_avg_ms, 4),
+                "algorithmic_flop_per_launch": dom_flops}
+
+    # ---- composite permute bandwidth (all P ranks' Q, K, V; not part of the step)
+    ys = {t: torch.empty((p, s_pad, full[t].shape[1] // p, d), dtype=torch.bfloat16, device=dev)
+          for t in (workloads.Q, workloads.K, workloads.V)}
+    nbytes = sum(full[t].numel() * 2 + ys[t].numel() * 2 for t in ys)
+
+    def pack_all():
+        for t in ys:
+            usp.usp_pad_pack_seq2head(full[t], p, out=ys[t])
+
+    for _ in range(3):
+        pack_all()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        pack_all()
+    e1.record()
+    torch.cuda.synchronize()
+    pack_ms = e0.elapsed_time(e1) / reps
+    permute_gbs = nbytes / (pack_ms * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round((f_fwd + f_bwd) / (step_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: one Ulysses rank's attention layer, S={w.s} "
+                               f"(s_pad {w.s_pad}), SP degree {p}, {hq} Q / {hkv} KV heads, "
+                               f"d={d}, causal, forward+backward, pack/unpack of the rank's slice",
+                   "seq_len": w.s, "sp_degree": p, "heads_q": hq, "heads_kv": hkv,
+                   "head_dim": d, "causal": True},
+        "attn_fwd_ms": round(fwd_ms, 3),
+        "attn_bwd_ms": round(bwd_ms, 3),
+        "attn_fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 1),
+        "attn_fwd_bwd_tflops": round((f_fwd + f_bwd) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 1),
+        "attn_fwd_frac_of_peak": round(f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "attn_fwd_bwd_frac_of_peak": round((f_fwd + f_bwd) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12
+                                           / PEAK_BF16_TFLOPS, 4),
+        "step_permute_ms": round(perm_ms, 4),
+        "permute_gbps": round(permute_gbs, 1),
+        "permute_frac_of_hbm_peak": round(permute_gbs / PEAK_HBM_GBS, 4),
+        "permute_bytes": nbytes,
+        "kernels_ms_per_step": {e["name"]: round(e["total_ms"] / args.steps, 4) for e in trace},
+        "wall_s_timed": round(t_wall, 3),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

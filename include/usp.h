@@ -1,0 +1,174 @@
+/*
+ * usp.h: C ABI of the Ulysses sequence-parallel rank-share hot path on
+ * MI355X (gfx950).
+ *
+ * What the calls compute. In Ulysses sequence parallelism each of P ranks
+ * holds one contiguous slice of the (padded) sequence with all heads. Separate
+ * all-to-alls of Q, K and V give every rank the full sequence restricted to its
+ * H/P heads; it runs ordinary attention locally and a reverse all-to-all returns
+ * the output to sequence slices ("feat(dspark): add Ulysses sequence parallel
+ * training", Motivation and Modifications: shard-and-pad, separate Q/K/V
+ * all-to-alls, head counts divisible by the Ulysses degree). On one device the
+ * P packs plus the all-to-all compose into usp_pad_pack_seq2head, the reverse
+ * into usp_unpack_head2seq, and usp_attn_fwd / usp_attn_bwd are one rank's
+ * local attention, forward and backward (same page, Accuracy Test: loss and
+ * gradient parity with full-sequence attention), with packed documents given by
+ * cu_seqlens ("GLM-5.2 131k context parallelism", Purpose: THD packed
+ * sequences).
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE memory owned by the caller; the library
+ *     never allocates device memory and keeps no state between calls (apart
+ *     from the optional kernel trace below).
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL means the default stream). The return value is known
+ *     synchronously: argument checks run on the host before any HIP call, so a
+ *     rejected call enqueues nothing.
+ *   - Tensor pointers must be 16-byte aligned; outputs may not overlap inputs.
+ *   - dtype is USP_BF16 (bfloat16 storage, fp32 accumulation) or USP_FP32.
+ *   - Errors are return codes only (usp_status); usp_status_string() names them.
+ */
+#ifndef USP_H_
+#define USP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  USP_OK = 0,
+  USP_ERR_INVALID = -1,     /* shape, divisibility, range, alignment or aliasing */
+  USP_ERR_UNSUPPORTED = -2, /* dtype / head dim not built */
+  USP_ERR_NULL = -3,        /* a required pointer is NULL */
+  USP_ERR_HIP = -4,         /* the HIP runtime reported a launch error */
+  USP_ERR_WORKSPACE = -5    /* workspace NULL or smaller than required */
+} usp_status;
+
+typedef enum { USP_BF16 = 0, USP_FP32 = 1 } usp_dtype;
+
+/* Library ABI version (major*100 + minor). */
+int usp_version(void);
+
+/* Human-readable name of a usp_status value (static string, never NULL). */
+const char* usp_status_string(int status);
+
+/*
+ * Padded sequence length for a Ulysses degree p: the smallest multiple of p
+ * that is >= s_real (alignment padding before sharding, "feat(dspark)",
+ * Modifications). Returns -1 if p < 1 or s_real < 0.
+ */
+int64_t usp_padded_len(int64_t s_real, int p);
+
+/*
+ * Pad + pack, sequence-sharded -> head-sharded ("feat(dspark)", Modifications:
+ * shard and pad, then the Q/K/V all-to-all). With hp = h / p and
+ * s_pad = usp_padded_len(s_real, p):
+ *     y[r][s][j][:] = x[s][r*hp + j][:]   for s <  s_real
+ *     y[r][s][j][:] = 0                   for s_real <= s < s_pad
+ *   x: [s_real][h][d] row-major, read only.
+ *   y: [p][s_pad][hp][d] row-major, fully overwritten (padding rows included).
+ * Bit-exact copy. Errors: USP_ERR_INVALID if h % p != 0, p < 1, h < 1, d < 1,
+ * s_real < 0, misaligned pointers, or overlap of x and y; USP_ERR_UNSUPPORTED
+ * if d * sizeof(elem) is not a multiple of 4 bytes; USP_ERR_NULL for NULL
+ * pointers when there is data. s_real = 0 writes nothing.
+ */
+int usp_pad_pack_seq2head(const void* x, void* y, int64_t s_real, int p, int h, int d,
+                          int dtype, void* stream);
+
+/*
+ * Unpack, head-sharded -> sequence-sharded: the inverse of the pack on the real
+ * rows, padding rows dropped (the reverse all-to-all that returns the attention
+ * output to each rank's slice).
+ *     x[s][r*hp + j][:] = y[r][s][j][:]   for s < s_real
+ *   y: [p][s_pad][hp][d] read only; x: [s_real][h][d] fully overwritten.
+ * Same errors as the pack.
+ */
+int usp_unpack_head2seq(const void* y, void* x, int64_t s_real, int p, int h, int d,
+                        int dtype, void* stream);
+
+/*
+ * Workspace bytes usp_attn_fwd needs (0 for USP_FP32). The bf16 path stores a
+ * key-major copy of V there.
+ */
+size_t usp_attn_fwd_workspace_bytes(int64_t s_pad, int hq, int hkv, int d, int dtype);
+
+/*
+ * Attention forward over one rank's share: the full (padded) sequence, hq query
+ * heads, hkv key/value heads, query head i reading key/value head i / (hq/hkv).
+ * For query row i the allowed keys are
+ *     M(i) = { j < s_valid, doc(j) == doc(i), and j <= i when causal }
+ * with doc() from cu_seqlens (one document when cu_seqlens is NULL). Then
+ *     lse[h][i] = log sum_{j in M(i)} exp(scale * q_i . k_j)   (natural log)
+ *     o[i][h]   = sum_{j in M(i)} exp(scale * q_i . k_j - lse[h][i]) v_j
+ * Padded query rows (i >= s_valid) are computed like any other row.
+ *   q: [s_pad][hq][d], k and v: [s_pad][hkv][d], read only.
+ *   o: [s_pad][hq][d] (dtype), lse: [hq][s_pad] fp32; both fully overwritten.
+ *   cu_seqlens: device int32 [n_docs + 1] with 0 = cu[0] <= ... <= cu[n_docs]
+ *     = s_pad, or NULL. Its contents are not checked (device memory); values
+ *     outside [0, s_pad] are clamped, never dereferenced out of range.
+ *   workspace: device memory of usp_attn_fwd_workspace_bytes() bytes (may be
+ *     NULL when that is 0); contents are scratch.
+ * Supported: d in {64, 128} for USP_FP32, d = 128 for USP_BF16.
+ * Errors: USP_ERR_INVALID for s_valid < 1 or > s_pad, hq % hkv != 0,
+ * cu_seqlens with s_valid != s_pad or n_docs < 1, misalignment, aliasing;
+ * USP_ERR_UNSUPPORTED for other d / dtype; USP_ERR_WORKSPACE if the workspace
+ * is too small.
+ */
+int usp_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 void* workspace, size_t workspace_bytes,
+                 int64_t s_pad, int64_t s_valid, const int32_t* cu_seqlens, int n_docs,
+                 int hq, int hkv, int d, float softmax_scale, int causal, int dtype,
+                 void* stream);
+
+/* Workspace bytes usp_attn_bwd needs for these sizes. */
+size_t usp_attn_bwd_workspace_bytes(int64_t s_pad, int hq, int hkv, int d, int dtype);
+
+/*
+ * Attention backward for the loss whose gradient with respect to o is dout
+ * (chain rule through the softmax; gradient parity in "feat(dspark)", Accuracy
+ * Test). With P_ij = exp(scale q_i.k_j - lse_i) on M(i), dP_ij = dout_i . v_j,
+ * D_i = sum_j P_ij dP_ij (taken as dout_i . o_i) and dS = P (dP - D):
+ *     dq_i = scale sum_j dS_ij k_j
+ *     dk_j = scale sum_{heads of the group} sum_i dS_ij q_i
+ *     dv_j = sum_{heads of the group} sum_i P_ij dout_i
+ *   q, o, dout: [s_pad][hq][d]; k, v: [s_pad][hkv][d]; lse: [hq][s_pad] fp32
+ *     as written by usp_attn_fwd; all read only.
+ *   dq: [s_pad][hq][d], dk and dv: [s_pad][hkv][d]; fully overwritten.
+ *   workspace: usp_attn_bwd_workspace_bytes() bytes of device scratch.
+ * Masks, supported sizes and errors as in usp_attn_fwd.
+ */
+int usp_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes,
+                 int64_t s_pad, int64_t s_valid, const int32_t* cu_seqlens, int n_docs,
+                 int hq, int hkv, int d, float softmax_scale, int causal, int dtype,
+                 void* stream);
+
+/*
+ * Kernel tracing (profiling aid, off by default). While enabled, every kernel
+ * the library launches is bracketed by a pair of HIP events recorded on its
+ * stream. usp_trace_collect() waits for the recorded events, returns per-kernel
+ * launch counts and summed durations (at most max_entries kernels, sorted by
+ * total time, descending), and clears the record. This is the only state the
+ * library keeps between calls.
+ *   usp_trace_enable returns the previous setting.
+ *   usp_trace_collect returns the number of entries written, or USP_ERR_NULL /
+ *   USP_ERR_HIP.
+ */
+typedef struct {
+  char name[48];
+  long long launches;
+  double total_ms;
+} usp_trace_entry;
+
+int usp_trace_enable(int on);
+int usp_trace_collect(usp_trace_entry* out, int max_entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* USP_H_ */

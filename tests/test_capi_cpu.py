@@ -1,0 +1,195 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point
+include/usp.h declares, and rejects bad arguments on the host before any HIP
+call (so these run without a GPU; no compute call is made)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "usp.h")
+
+OK, INVALID, UNSUPPORTED, NULLP, HIPERR, WORKSPACE = 0, -1, -2, -3, -4, -5
+BF16, FP32 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def L():
+    import ulysses_sequence_parallelism_amd as usp
+    if not os.path.exists(usp.LIB_PATH):
+        pytest.skip("libusp.so not built")
+    return usp.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(usp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_hot_path_calls():
+    names = declared_functions()
+    for n in ("usp_pad_pack_seq2head", "usp_attn_fwd", "usp_attn_bwd", "usp_unpack_head2seq"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    import ulysses_sequence_parallelism_amd as usp
+    out = subprocess.run(["nm", "-D", "--defined-only", usp.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (usp_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+    # and the Python binding has a function of the same name
+    for name in declared_functions():
+        assert callable(getattr(usp, name)), name
+
+
+def test_version_and_status_strings(L):
+    assert L.usp_version() == 100
+    for s in (OK, INVALID, UNSUPPORTED, NULLP, HIPERR, WORKSPACE, 12345):
+        assert isinstance(L.usp_status_string(s), bytes)
+    assert L.usp_status_string(0) == b"ok"
+
+
+def test_padded_len_matches_oracle(L):
+    for s in list(range(0, 40)) + [119999, 120000, 131071]:
+        for p in (1, 2, 3, 4, 8):
+            assert L.usp_padded_len(s, p) == oracle.padded_len(s, p)
+    assert L.usp_padded_len(5, 0) == -1
+    assert L.usp_padded_len(-1, 2) == -1
+
+
+A = 1 << 20  # fake, 16-byte-aligned addresses: never dereferenced by a rejected call
+B = 1 << 40
+
+
+def pack(L, x, y, s, p, h, d, dt):
+    return L.usp_pad_pack_seq2head(ctypes.c_void_p(x), ctypes.c_void_p(y), s, p, h, d, dt, None)
+
+
+def unpack(L, y, x, s, p, h, d, dt):
+    return L.usp_unpack_head2seq(ctypes.c_void_p(y), ctypes.c_void_p(x), s, p, h, d, dt, None)
+
+
+def test_permute_argument_errors(L):
+    for f in (pack, unpack):
+        assert f(L, A, B, 16, 3, 8, 128, BF16) == INVALID       # heads not divisible
+        assert f(L, A, B, 16, 0, 8, 128, BF16) == INVALID       # p < 1
+        assert f(L, A, B, -1, 2, 8, 128, BF16) == INVALID       # s < 0
+        assert f(L, A, B, 16, 2, 8, 0, BF16) == INVALID         # d < 1
+        assert f(L, A, B, 16, 2, 8, 128, 7) == UNSUPPORTED      # dtype
+        assert f(L, A, B, 16, 2, 2, 1, BF16) == UNSUPPORTED     # 2-byte runs
+        assert f(L, A + 8, B, 16, 2, 8, 128, BF16) == INVALID   # misaligned
+        assert f(L, A, B + 4, 16, 2, 8, 128, BF16) == INVALID
+        assert f(L, 0, B, 16, 2, 8, 128, BF16) == NULLP
+        assert f(L, A, 0, 16, 2, 8, 128, BF16) == NULLP
+        assert f(L, A, A + 4096, 16, 2, 8, 128, BF16) == INVALID  # overlap
+        assert f(L, A, B, 0, 2, 8, 128, BF16) == OK             # nothing to do, no HIP call
+        assert f(L, 0, 0, 0, 2, 8, 128, FP32) == OK
+
+
+def fwd(L, s_pad=256, s_valid=256, cu=None, n_docs=0, hq=4, hkv=1, d=128, scale=0.088, causal=1,
+        dt=BF16, ws=3 << 30, ws_bytes=1 << 30, ptrs=None):
+    q, k, v, o, lse = ptrs or (A, A + (1 << 24), A + (2 << 24), A + (3 << 24), A + (4 << 24))
+    return L.usp_attn_fwd(*(ctypes.c_void_p(x) for x in (q, k, v, o, lse, ws)), ws_bytes, s_pad,
+                          s_valid, ctypes.c_void_p(cu), n_docs, hq, hkv, d, scale, causal, dt,
+                          None)
+
+
+def bwd(L, s_pad=256, s_valid=256, cu=None, n_docs=0, hq=4, hkv=1, d=128, scale=0.088, causal=1,
+        dt=BF16, ws=3 << 30, ws_bytes=1 << 30, ptrs=None):
+    base = [A + (i << 24) for i in range(9)]
+    ptrs = ptrs or base
+    return L.usp_attn_bwd(*(ctypes.c_void_p(x) for x in ptrs), ctypes.c_void_p(ws), ws_bytes,
+                          s_pad, s_valid, ctypes.c_void_p(cu), n_docs, hq, hkv, d, scale, causal,
+                          dt, None)
+
+
+@pytest.mark.parametrize("f", [fwd, bwd])
+def test_attention_argument_errors(L, f):
+    assert f(L, hq=6, hkv=4) == INVALID                 # hq % hkv
+    assert f(L, s_valid=0) == INVALID
+    assert f(L, s_valid=257) == INVALID
+    assert f(L, s_pad=0, s_valid=0) == INVALID
+    assert f(L, cu=A + (8 << 24), n_docs=2, s_valid=250) == INVALID  # packed docs + padding
+    assert f(L, cu=A + (8 << 24), n_docs=0) == INVALID
+    assert f(L, cu=A + (8 << 24) + 2, n_docs=2) == INVALID            # misaligned offsets
+    assert f(L, d=64) == UNSUPPORTED                    # bf16 is built for d = 128
+    assert f(L, d=96, dt=FP32) == UNSUPPORTED
+    assert f(L, dt=3) == UNSUPPORTED
+    assert f(L, scale=0.0) == INVALID
+    assert f(L, scale=float("nan")) == INVALID
+    assert f(L, causal=2) == INVALID
+    assert f(L, ws=0) == WORKSPACE
+    assert f(L, ws_bytes=16) == WORKSPACE
+    assert f(L, ws=(3 << 30) + 8) == INVALID            # misaligned workspace
+
+
+def test_attention_null_and_alias(L):
+    z = [A + (i << 24) for i in range(9)]
+    assert fwd(L, ptrs=(0, z[1], z[2], z[3], z[4])) == NULLP
+    assert fwd(L, ptrs=(z[0], z[1], z[2], z[0] + 1024, z[4])) == INVALID  # o overlaps q
+    assert fwd(L, ptrs=(z[0], z[1], z[2], z[3], z[3] + 64)) == INVALID    # lse overlaps o
+    assert fwd(L, ws=z[0]) == INVALID                                     # workspace overlaps q
+    p = list(z)
+    p[6] = p[0]  # dq aliases q
+    assert bwd(L, ptrs=p) == INVALID
+    p = list(z)
+    p[8] = p[7]  # dv aliases dk
+    assert bwd(L, ptrs=p) == INVALID
+    p = list(z)
+    p[5] = 0
+    assert bwd(L, ptrs=p) == NULLP
+
+
+def test_workspace_sizes(L):
+    for s in (1, 100, 128, 129, 120000, 131072):
+        f = L.usp_attn_fwd_workspace_bytes(s, 4, 1, 128, BF16)
+        b = L.usp_attn_bwd_workspace_bytes(s, 4, 1, 128, BF16)
+        assert f >= 128 * s * 2 and f % 16 == 0
+        assert b >= (2 * 4 + 1) * 128 * s * 2 + 4 * s * 4
+    assert L.usp_attn_fwd_workspace_bytes(512, 4, 2, 64, FP32) == 0
+    assert L.usp_attn_bwd_workspace_bytes(512, 4, 2, 64, FP32) == 512 * 4 * 4
+    assert L.usp_attn_fwd_workspace_bytes(0, 4, 1, 128, BF16) == 0
+
+
+def test_fast_division_host_side(tmp_path):
+    """The pack/unpack kernels divide by run and row lengths with a
+    multiply-high reciprocal; check it exhaustively on small values and on
+    random 32-bit values, on the host."""
+    src = tmp_path / "fastdiv.cpp"
+    src.write_text(r'''
+#include "usp_internal.h"
+#include <cstdio>
+#include <random>
+int main() {
+  std::mt19937_64 g(1);
+  for (uint32_t d = 1; d < 5000; ++d) {
+    usp::FastDiv f = usp::FastDiv::make(d);
+    for (uint32_t n = 0; n < 20000; ++n) if (f.div(n) != n / d) { printf("bad %u %u\n", n, d); return 1; }
+    for (int t = 0; t < 2000; ++t) { uint32_t n = (uint32_t)g(); if (f.div(n) != n / d) { printf("bad %u %u\n", n, d); return 1; } }
+  }
+  for (int t = 0; t < 200000; ++t) {
+    uint32_t d = (uint32_t)(g() % 0x7fffffffu) + 1, n = (uint32_t)g();
+    if (usp::FastDiv::make(d).div(n) != n / d) { printf("bad %u %u\n", n, d); return 1; }
+  }
+  printf("ok\n");
+  return 0;
+}
+''')
+    exe = tmp_path / "fastdiv"
+    inc = os.path.join(ROOT, "ulysses_sequence_parallelism_amd", "csrc")
+    hipcc = "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    subprocess.run([hipcc, "-O2", "-std=c++17", "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", inc,
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True,
+                   capture_output=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout

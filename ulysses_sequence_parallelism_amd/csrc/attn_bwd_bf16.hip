@@ -1,0 +1,510 @@
+// Attention backward, bf16 in / fp32 accumulate, d = 128, gfx950 matrix cores.
+//
+// Gradients of one rank's local attention ("feat(dspark): add Ulysses sequence
+// parallel training", Accuracy Test: loss and gradient parity with full-sequence
+// attention). With the saved natural-log LSE, P_ij = exp(scale q_i.k_j - LSE_i)
+// on the allowed keys, dP_ij = dO_i.v_j, D_i = dO_i.O_i, dS = P (dP - D):
+//     dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO
+// with dK and dV summed over the query heads that share a key/value head.
+//
+// Design (gfx950): two matrix-core kernels, each with one operand stationary
+// in registers, so neither needs atomics and both are deterministic.
+//   * dK/dV kernel (key-stationary): a workgroup owns 128 keys of one KV head
+//     (32 per wave; K and V fragments live in registers) and walks every query
+//     tile of every query head of the group that can see them. Scores are
+//     computed as S = Q K^T so a lane owns one KEY: P and dS go from the
+//     accumulators straight into the B operand of dV^T += dO^T P and
+//     dK^T += Q^T dS, whose A operands are key-major Q / dO copies in LDS.
+//   * dQ kernel (query-stationary): like the forward, S^T = K Q^T and
+//     dP^T = V dO^T with Q and dO in registers; a lane owns one QUERY, so LSE
+//     and D are per-lane scalars, and dS^T feeds dQ^T += K^T dS^T directly.
+//   * The cost of skipping atomics is recomputing S and dP in the dQ kernel
+//     (7 GEMMs of the 5 the method needs); in exchange there is no fp32
+//     accumulation traffic through L2 and the result is reproducible.
+//   * Preprocess: D = rowsum(dO * O) and the key-major copies of Q, dO, K.
+//   * Tiles are double-buffered in LDS with padded pitches, masks are applied
+//     only on boundary tiles, and the causal triangle is launched
+//     heaviest-first.
+#include "usp_common.h"
+#include "usp_internal.h"
+
+namespace usp {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int KP = D + 8;    // row-major tile pitch (elements)
+constexpr int TP = 64 + 8;   // key-major tile pitch (elements)
+
+// ---------------------------------------------------------------------------
+// D_i = sum_d dO[i][h][d] * O[i][h][d]  (fp32 from the bf16 values)
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const __bf16* __restrict__ o,
+                                                         const __bf16* __restrict__ dout,
+                                                         float* __restrict__ dd, int s_pad,
+                                                         int hq, int64_t s_t) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 16 lanes per (row, head)
+  const int64_t rh = t >> 4;
+  const int part = (int)(t & 15);
+  float s = 0.f;
+  const bool live = rh < (int64_t)s_pad * hq;
+  if (live) {
+    u32x4 a = *reinterpret_cast<const u32x4*>(o + rh * D + part * 8);
+    u32x4 b = *reinterpret_cast<const u32x4*>(dout + rh * D + part * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s += bf16_bits_to_f32((unsigned short)(a[e] & 0xffff)) * bf16_bits_to_f32((unsigned short)(b[e] & 0xffff));
+      s += bf16_bits_to_f32((unsigned short)(a[e] >> 16)) * bf16_bits_to_f32((unsigned short)(b[e] >> 16));
+    }
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 16);
+  if (live && part == 0) {
+    const int i = (int)(rh / hq), h = (int)(rh % hq);
+    dd[(int64_t)h * s_t + i] = s;
+  }
+}
+
+struct BwdParams {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* dout;
+  const __bf16* qt;    // key-major Q   [hq][D][s_t]
+  const __bf16* dot;   // key-major dO  [hq][D][s_t]
+  const __bf16* kt;    // key-major K   [hkv][D][s_t]
+  const float* lse;    // [hq][s_pad]
+  const float* dd;     // [hq][s_t]
+  __bf16* dq;
+  __bf16* dk;
+  __bf16* dv;
+  const int32_t* cu;
+  int64_t s_t;
+  int s_pad, s_valid, n_docs, hq, hkv, causal, n_blocks;
+  float scale, scale_log2;
+};
+
+// ---------------------------------------------------------------------------
+// dK / dV: key-stationary. Workgroup = 4 waves x 32 keys of one KV head.
+constexpr int BQ = 64;  // query rows per tile
+
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams pr) {
+  __shared__ __attribute__((aligned(16))) __bf16 lq[2][BQ * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 ldo[2][BQ * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 lqt[2][D * TP];
+  __shared__ __attribute__((aligned(16))) __bf16 ldot[2][D * TP];
+  __shared__ __attribute__((aligned(16))) float llse[2][BQ];
+  __shared__ __attribute__((aligned(16))) float ldd[2][BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hl = lane >> 5, ln = lane & 31;
+  const int s_pad = pr.s_pad, s_valid = pr.s_valid, causal = pr.causal;
+  const int g = pr.hq / pr.hkv;
+  const int kvh = blockIdx.y;
+  const int j0 = blockIdx.x * 128;
+  const int j1 = min(j0 + 128, s_pad);
+  const int wj0 = j0 + w * 32;
+  const int key = wj0 + ln;
+  const int kc = min(key, s_pad - 1);
+
+  // this lane's key: rows [rlo, rhi) may see it
+  const DocBounds kb_ = doc_bounds(pr.cu, pr.n_docs, kc, s_pad);
+  const bool key_ok = key < s_valid;
+  const int rlo = max(kb_.lo, causal ? key : 0);
+  const int rhi = kb_.hi;
+  // workgroup row range and mask-free test
+  const DocBounds dfirst = doc_bounds(pr.cu, pr.n_docs, j0, s_pad);
+  const DocBounds dlast = doc_bounds(pr.cu, pr.n_docs, j1 - 1, s_pad);
+  const int rstart = causal ? j0 : dfirst.lo;
+  const int rend = dlast.hi - 1;
+  const int free_lo = max(dlast.lo, causal ? j1 - 1 : 0);
+  const int free_hi = dfirst.hi - 1;
+  const bool all_keys_valid = j1 - 1 < s_valid;
+  // this wave's row range
+  const int wlast = min(wj0 + 31, s_pad - 1);
+  const bool wave_live = wj0 < s_pad && wj0 < s_valid;
+  const int wr_lo = causal ? wj0 : doc_bounds(pr.cu, pr.n_docs, min(wj0, s_pad - 1), s_pad).lo;
+  const int wr_hi = doc_bounds(pr.cu, pr.n_docs, wlast, s_pad).hi - 1;
+
+  // stationary K and V fragments (B operands), lane = key
+  bf16x8 kreg[8], vreg[8];
+  {
+    const int64_t off = ((int64_t)kc * pr.hkv + kvh) * D + hl * 8;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      kreg[kk] = *reinterpret_cast<const bf16x8*>(pr.k + off + kk * 16);
+      vreg[kk] = *reinterpret_cast<const bf16x8*>(pr.v + off + kk * 16);
+    }
+  }
+  f32x16 dka[4], dva[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    dka[b] = f32x16{};
+    dva[b] = f32x16{};
+  }
+
+  const int tstart = (rstart / BQ) * BQ;
+  const int ntr = (j0 < s_valid && rend >= rstart) ? (rend - tstart) / BQ + 1 : 0;
+  const int nt = ntr * g;
+
+  u32x4 sq[4], sdo[4], sqt[4], sdot[4];
+  float slse = 0.f, sdd = 0.f;
+  auto load_tile = [&](int it) {
+    const int h = kvh * g + it / ntr;
+    const int r0 = tstart + (it % ntr) * BQ;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = (tid >> 4) + 16 * u, c = tid & 15;
+      const int i = r0 + r;
+      const int64_t off = ((int64_t)i * pr.hq + h) * D + c * 8;
+      sq[u] = i < s_pad ? *reinterpret_cast<const u32x4*>(pr.q + off) : u32x4{0u, 0u, 0u, 0u};
+      sdo[u] = i < s_pad ? *reinterpret_cast<const u32x4*>(pr.dout + off) : u32x4{0u, 0u, 0u, 0u};
+      const int dr = (tid >> 3) + 32 * u, c8 = tid & 7;
+      const int64_t toff = ((int64_t)h * D + dr) * pr.s_t + r0 + c8 * 8;
+      sqt[u] = *reinterpret_cast<const u32x4*>(pr.qt + toff);
+      sdot[u] = *reinterpret_cast<const u32x4*>(pr.dot + toff);
+    }
+    if (tid < BQ) {
+      const int i = r0 + tid;
+      slse = i < s_pad ? pr.lse[(int64_t)h * s_pad + i] * kLog2e : 0.f;
+      sdd = i < s_pad ? pr.dd[(int64_t)h * pr.s_t + i] : 0.f;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = (tid >> 4) + 16 * u, c = tid & 15;
+      *reinterpret_cast<u32x4*>(&lq[buf][r * KP + c * 8]) = sq[u];
+      *reinterpret_cast<u32x4*>(&ldo[buf][r * KP + c * 8]) = sdo[u];
+      const int dr = (tid >> 3) + 32 * u, c8 = tid & 7;
+      *reinterpret_cast<u32x4*>(&lqt[buf][dr * TP + c8 * 8]) = sqt[u];
+      *reinterpret_cast<u32x4*>(&ldot[buf][dr * TP + c8 * 8]) = sdot[u];
+    }
+    if (tid < BQ) {
+      llse[buf][tid] = slse;
+      ldd[buf][tid] = sdd;
+    }
+  };
+
+  if (nt > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < nt; ++it) {
+    const int buf = it & 1;
+    const int r0 = tstart + (it % ntr) * BQ;
+    if (it + 1 < nt) load_tile(it + 1);
+
+    if (wave_live && r0 + BQ - 1 >= wr_lo && r0 <= wr_hi) {
+      // S = Q K^T and dP = dO V^T: rows = queries (two 32-row blocks), cols = keys
+      f32x16 sa[2] = {f32x16{}, f32x16{}}, pa[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const __bf16* qp = &lq[buf][(mb * 32 + ln) * KP + hl * 8];
+        const __bf16* dp = &ldo[buf][(mb * 32 + ln) * KP + hl * 8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          sa[mb] = mfma32(*reinterpret_cast<const bf16x8*>(qp + kk * 16), kreg[kk], sa[mb]);
+          pa[mb] = mfma32(*reinterpret_cast<const bf16x8*>(dp + kk * 16), vreg[kk], pa[mb]);
+        }
+      }
+      const bool full = all_keys_valid && r0 >= free_lo && r0 + BQ - 1 <= free_hi;
+      bf16x8 pt[4], dst[4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int rr = mb * 32 + r4 * 8 + hl * 4;  // first of 4 consecutive rows
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&llse[buf][rr]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&ldd[buf][rr]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = r4 * 4 + e;
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[mb][i], pr.scale_log2, -l4[e]));
+            if (!full) {
+              const int row = r0 + rr + e;
+              if (!(key_ok && row >= rlo && row < rhi)) p = 0.f;
+            }
+            sa[mb][i] = p;
+            pa[mb][i] = p * (pa[mb][i] - d4[e]);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          u32x4 a, b;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            a[t] = pack_bf16x2(sa[mb][8 * c + 2 * t], sa[mb][8 * c + 2 * t + 1]);
+            b[t] = pack_bf16x2(pa[mb][8 * c + 2 * t], pa[mb][8 * c + 2 * t + 1]);
+          }
+          pt[mb * 2 + c] = __builtin_bit_cast(bf16x8, a);
+          dst[mb * 2 + c] = __builtin_bit_cast(bf16x8, b);
+        }
+      }
+      // dV^T += dO^T P,  dK^T += Q^T dS  (rows = d, cols = keys)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const __bf16* op = &ldot[buf][(b * 32 + ln) * TP + hl * 8];
+        const __bf16* qp = &lqt[buf][(b * 32 + ln) * TP + hl * 8];
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+          dva[b] = mfma32(*reinterpret_cast<const bf16x8*>(op + ch * 16), pt[ch], dva[b]);
+          dka[b] = mfma32(*reinterpret_cast<const bf16x8*>(qp + ch * 16), dst[ch], dka[b]);
+        }
+      }
+    }
+    if (it + 1 < nt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (key < s_pad) {
+    __bf16* kp = pr.dk + ((int64_t)key * pr.hkv + kvh) * D + hl * 4;
+    __bf16* vp = pr.dv + ((int64_t)key * pr.hkv + kvh) * D + hl * 4;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        u32x2 k2 = {pack_bf16x2(dka[b][4 * r] * pr.scale, dka[b][4 * r + 1] * pr.scale),
+                    pack_bf16x2(dka[b][4 * r + 2] * pr.scale, dka[b][4 * r + 3] * pr.scale)};
+        u32x2 v2 = {pack_bf16x2(dva[b][4 * r], dva[b][4 * r + 1]),
+                    pack_bf16x2(dva[b][4 * r + 2], dva[b][4 * r + 3])};
+        *reinterpret_cast<u32x2*>(kp + b * 32 + r * 8) = k2;
+        *reinterpret_cast<u32x2*>(vp + b * 32 + r * 8) = v2;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: query-stationary. Workgroup = 4 waves sharing one KV head (HG heads x
+// 4/HG blocks of 32 query rows), as in the forward.
+constexpr int BN = 64;  // keys per tile
+
+template <int HG>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams pr) {
+  constexpr int QROWS = 32 * (4 / HG);
+  __shared__ __attribute__((aligned(16))) __bf16 lk[2][BN * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 lv[2][BN * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 lkt[2][D * TP];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hl = lane >> 5, ln = lane & 31;
+  const int s_pad = pr.s_pad, s_valid = pr.s_valid, causal = pr.causal;
+  const int g = pr.hq / pr.hkv;
+  const int chunks = g / HG;
+  const int kvh = blockIdx.y / chunks, hc = blockIdx.y % chunks;
+  const int head = kvh * g + hc * HG + (w % HG);
+  const int qb = pr.n_blocks - 1 - (int)blockIdx.x;
+  const int q0 = qb * QROWS;
+  const int q1 = min(q0 + QROWS, s_pad);
+  const int wq0 = q0 + (w / HG) * 32;
+  const int qi = wq0 + ln;
+  const bool row_ok = qi < s_pad;
+  const int qc = row_ok ? qi : s_pad - 1;
+
+  const DocBounds db = doc_bounds(pr.cu, pr.n_docs, qc, s_pad);
+  const int lo = db.lo;
+  const int hi = causal ? min(qc, s_valid - 1) : min(db.hi, s_valid) - 1;
+  const DocBounds dfirst = doc_bounds(pr.cu, pr.n_docs, q0, s_pad);
+  const DocBounds dlast = doc_bounds(pr.cu, pr.n_docs, q1 - 1, s_pad);
+  const int kmin = dfirst.lo;
+  const int kmax = causal ? min(q1 - 1, s_valid - 1) : min(dlast.hi, s_valid) - 1;
+  const int free_lo = dlast.lo;
+  const int free_hi = causal ? min(q0, s_valid - 1) : min(dfirst.hi, s_valid) - 1;
+  const int wlast = min(wq0 + 31, s_pad - 1);
+  const int wkmin = doc_bounds(pr.cu, pr.n_docs, min(wq0, s_pad - 1), s_pad).lo;
+  const int wkmax = causal ? min(wlast, s_valid - 1)
+                           : min(doc_bounds(pr.cu, pr.n_docs, wlast, s_pad).hi, s_valid) - 1;
+
+  bf16x8 qreg[8], doreg[8];
+  {
+    const int64_t off = ((int64_t)qc * pr.hq + head) * D + hl * 8;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      qreg[kk] = *reinterpret_cast<const bf16x8*>(pr.q + off + kk * 16);
+      doreg[kk] = *reinterpret_cast<const bf16x8*>(pr.dout + off + kk * 16);
+    }
+  }
+  const float lse2 = pr.lse[(int64_t)head * s_pad + qc] * kLog2e;
+  const float drow = pr.dd[(int64_t)head * pr.s_t + qc];
+
+  f32x16 dqa[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) dqa[b] = f32x16{};
+
+  const int tstart = (kmin / BN) * BN;
+  const int nt = kmax >= kmin ? (kmax - tstart) / BN + 1 : 0;
+
+  u32x4 sk[4], sv[4], skt[4];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = (tid >> 4) + 16 * u, c = tid & 15;
+      const int j = t0 + r;
+      const int64_t off = ((int64_t)j * pr.hkv + kvh) * D + c * 8;
+      sk[u] = j < s_pad ? *reinterpret_cast<const u32x4*>(pr.k + off) : u32x4{0u, 0u, 0u, 0u};
+      sv[u] = j < s_pad ? *reinterpret_cast<const u32x4*>(pr.v + off) : u32x4{0u, 0u, 0u, 0u};
+      const int dr = (tid >> 3) + 32 * u, c8 = tid & 7;
+      skt[u] = *reinterpret_cast<const u32x4*>(pr.kt + ((int64_t)kvh * D + dr) * pr.s_t + t0 + c8 * 8);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = (tid >> 4) + 16 * u, c = tid & 15;
+      *reinterpret_cast<u32x4*>(&lk[buf][r * KP + c * 8]) = sk[u];
+      *reinterpret_cast<u32x4*>(&lv[buf][r * KP + c * 8]) = sv[u];
+      const int dr = (tid >> 3) + 32 * u, c8 = tid & 7;
+      *reinterpret_cast<u32x4*>(&lkt[buf][dr * TP + c8 * 8]) = skt[u];
+    }
+  };
+
+  if (nt > 0) {
+    load_tile(tstart);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < nt; ++it) {
+    const int t0 = tstart + it * BN;
+    const int buf = it & 1;
+    if (it + 1 < nt) load_tile(t0 + BN);
+
+    if (t0 <= wkmax && t0 + BN - 1 >= wkmin) {
+      f32x16 sa[2] = {f32x16{}, f32x16{}}, pa[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const __bf16* kp = &lk[buf][(kb * 32 + ln) * KP + hl * 8];
+        const __bf16* vp = &lv[buf][(kb * 32 + ln) * KP + hl * 8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          sa[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kp + kk * 16), qreg[kk], sa[kb]);
+          pa[kb] = mfma32(*reinterpret_cast<const bf16x8*>(vp + kk * 16), doreg[kk], pa[kb]);
+        }
+      }
+      const bool full = t0 >= free_lo && t0 + BN - 1 <= free_hi;
+      bf16x8 dst[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[kb][i], pr.scale_log2, -lse2));
+          if (!full) {
+            const int key = t0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+            if (key < lo || key > hi) p = 0.f;
+          }
+          pa[kb][i] = p * (pa[kb][i] - drow);
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          u32x4 b;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) b[t] = pack_bf16x2(pa[kb][8 * c + 2 * t], pa[kb][8 * c + 2 * t + 1]);
+          dst[kb * 2 + c] = __builtin_bit_cast(bf16x8, b);
+        }
+      }
+      // dQ^T += K^T dS^T (rows = d, cols = queries)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const __bf16* tp = &lkt[buf][(b * 32 + ln) * TP + hl * 8];
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch)
+          dqa[b] = mfma32(*reinterpret_cast<const bf16x8*>(tp + ch * 16), dst[ch], dqa[b]);
+      }
+    }
+    if (it + 1 < nt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (row_ok) {
+    __bf16* op = pr.dq + ((int64_t)qi * pr.hq + head) * D + hl * 4;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        u32x2 v2 = {pack_bf16x2(dqa[b][4 * r] * pr.scale, dqa[b][4 * r + 1] * pr.scale),
+                    pack_bf16x2(dqa[b][4 * r + 2] * pr.scale, dqa[b][4 * r + 3] * pr.scale)};
+        *reinterpret_cast<u32x2*>(op + b * 32 + r * 8) = v2;
+      }
+  }
+}
+
+template <int HG>
+int launch_dq(const BwdParams& p, int g, hipStream_t stream) {
+  constexpr int QROWS = 32 * (4 / HG);
+  BwdParams pr = p;
+  pr.n_blocks = (p.s_pad + QROWS - 1) / QROWS;
+  dim3 grid((unsigned)pr.n_blocks, (unsigned)(p.hkv * (g / HG)));
+  TraceScope ts("attn_bwd_dq_bf16", stream);
+  hipLaunchKernelGGL((bwd_dq_kernel<HG>), grid, dim3(256), 0, stream, pr);
+  return hipGetLastError() == hipSuccess ? USP_OK : USP_ERR_HIP;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+size_t attn_bwd_bf16_workspace(int64_t s_pad, int hq, int hkv, int d) {
+  const size_t s_t = (size_t)kmajor_len(s_pad);
+  return align256((size_t)hq * d * s_t * 2) * 2 + align256((size_t)hkv * d * s_t * 2) +
+         align256((size_t)hq * s_t * 4);
+}
+
+int attn_bwd_bf16(const AttnArgs& a) {
+  const int64_t s_t = kmajor_len(a.s_pad);
+  char* ws = static_cast<char*>(a.workspace);
+  const size_t qt_bytes = align256((size_t)a.hq * D * s_t * 2);
+  const size_t kt_bytes = align256((size_t)a.hkv * D * s_t * 2);
+  __bf16* qt = reinterpret_cast<__bf16*>(ws);
+  __bf16* dot = reinterpret_cast<__bf16*>(ws + qt_bytes);
+  __bf16* kt = reinterpret_cast<__bf16*>(ws + 2 * qt_bytes);
+  float* dd = reinterpret_cast<float*>(ws + 2 * qt_bytes + kt_bytes);
+
+  int rc = kmajor_launch(a.q, qt, a.s_pad, a.hq, s_t, a.stream, "attn_bwd_kmajor");
+  if (rc == USP_OK) rc = kmajor_launch(a.dout, dot, a.s_pad, a.hq, s_t, a.stream, "attn_bwd_kmajor");
+  if (rc == USP_OK) rc = kmajor_launch(a.k, kt, a.s_pad, a.hkv, s_t, a.stream, "attn_bwd_kmajor");
+  if (rc != USP_OK) return rc;
+  {
+    const int64_t n = a.s_pad * a.hq * 16;
+    TraceScope ts("attn_bwd_rowdot_bf16", a.stream);
+    hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, a.stream,
+                       static_cast<const __bf16*>(a.o), static_cast<const __bf16*>(a.dout), dd,
+                       (int)a.s_pad, a.hq, s_t);
+    if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
+  }
+  BwdParams p{};
+  p.q = static_cast<const __bf16*>(a.q);
+  p.k = static_cast<const __bf16*>(a.k);
+  p.v = static_cast<const __bf16*>(a.v);
+  p.dout = static_cast<const __bf16*>(a.dout);
+  p.qt = qt;
+  p.dot = dot;
+  p.kt = kt;
+  p.lse = a.lse;
+  p.dd = dd;
+  p.dq = static_cast<__bf16*>(a.dq);
+  p.dk = static_cast<__bf16*>(a.dk);
+  p.dv = static_cast<__bf16*>(a.dv);
+  p.cu = a.cu;
+  p.s_t = s_t;
+  p.s_pad = (int)a.s_pad;
+  p.s_valid = (int)a.s_valid;
+  p.n_docs = a.n_docs;
+  p.hq = a.hq;
+  p.hkv = a.hkv;
+  p.causal = a.causal;
+  p.scale = a.scale;
+  p.scale_log2 = a.scale * kLog2e;
+  {
+    dim3 grid((unsigned)((a.s_pad + 127) / 128), (unsigned)a.hkv);
+    TraceScope ts("attn_bwd_dkdv_bf16", a.stream);
+    hipLaunchKernelGGL(bwd_dkdv_kernel, grid, dim3(256), 0, a.stream, p);
+    if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
+  }
+  const int g = a.hq / a.hkv;
+  if (g % 4 == 0) return launch_dq<4>(p, g, a.stream);
+  if (g % 2 == 0) return launch_dq<2>(p, g, a.stream);
+  return launch_dq<1>(p, g, a.stream);
+}
+
+}  // namespace usp

@@ -1,0 +1,282 @@
+// Attention forward, bf16 in / fp32 accumulate, d = 128, gfx950 matrix cores.
+//
+// One rank's share of Ulysses attention is exact softmax attention over the
+// whole sequence for hq query heads sharing hkv key/value heads ("feat(dspark):
+// add Ulysses sequence parallel training", Modifications: local attention after
+// the Q/K/V all-to-alls, Q and KV head counts handled separately). Query row i
+// may use key j iff j < s_valid, doc(j) == doc(i) and j <= i when causal
+// (packed documents: "GLM-5.2 131k context parallelism", Purpose). The kernel
+// returns O and the natural-log LSE of every row.
+//
+// Design (gfx950):
+//   * Workgroup = 4 waves that share one KV head: HG query heads of the group
+//     times 4/HG blocks of 32 query rows. Each staged K/V tile feeds every
+//     wave, so a K/V byte brought into LDS serves 4*32 query rows.
+//   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+//     a lane then owns ONE query row (column l%32) and 16 keys per 32-key
+//     block, so the softmax row max / row sum are in-lane reductions plus one
+//     v_permlane32_swap across the two half-waves, and the row statistics
+//     (running max, sum, mask bounds) are per-lane scalars.
+//   * The probabilities go straight from the accumulator into the B operand of
+//     O^T += V^T P^T (no LDS round trip); V is staged from a key-major copy
+//     whose 16-key chunks are reordered to match (see kmajor.hip).
+//   * Q stays in registers for the whole key loop (8 x 16 bytes per lane).
+//   * K and V^T tiles of 64 keys are double-buffered in LDS (padded pitches:
+//     every 8-lane group of a 16-byte LDS read hits distinct banks); the next
+//     tile's global loads are issued before the current tile's math, one
+//     barrier per tile.
+//   * Online softmax in the log2 domain (scale*log2(e) folded into one FMA
+//     before v_exp_f32) with a lazy, exact rescale: the running max is only
+//     raised when a row's tile max exceeds it by more than 8 (log2 units), so
+//     probabilities stay <= 2^8 and the O rescale is skipped on almost every
+//     tile; the final normalisation uses the same running max, so nothing is
+//     approximated.
+//   * Causal / document / padding masks are applied only on tiles that cross
+//     a boundary; tiles entirely outside every row's range are never visited.
+//   * Workgroups are launched heaviest-first (last query block first) so the
+//     causal triangle's long rows start early and the tail is short.
+#include "usp_common.h"
+#include "usp_internal.h"
+
+namespace usp {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int BN = 64;        // keys per tile
+constexpr int KP = D + 8;     // K tile pitch (elements): 272 bytes
+constexpr int VP = BN + 8;    // V^T tile pitch (elements): 144 bytes
+constexpr float kRescaleThreshold = 8.0f;
+
+struct FwdParams {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* vt;   // key-major V: [hkv][D][s_t], 16-chunk reordered
+  __bf16* o;
+  float* lse;
+  const int32_t* cu;
+  int64_t s_t;
+  int s_pad, s_valid, n_docs, hq, hkv, causal, n_qblocks;
+  float scale_log2;   // softmax scale * log2(e)
+};
+
+template <int HG>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams pr) {
+  constexpr int QBW = 4 / HG;
+  constexpr int QROWS = 32 * QBW;
+  __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][BN * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][D * VP];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hl = lane >> 5, ln = lane & 31;
+  const int g = pr.hq / pr.hkv;
+  const int chunks = g / HG;
+  const int kvh = blockIdx.y / chunks, hc = blockIdx.y % chunks;
+  const int head = kvh * g + hc * HG + (w % HG);
+  const int qb = pr.n_qblocks - 1 - (int)blockIdx.x;  // heaviest first
+  const int q0 = qb * QROWS;
+  const int q1 = min(q0 + QROWS, pr.s_pad);
+  const int wq0 = q0 + (w / HG) * 32;
+  const int qi = wq0 + ln;
+  const bool row_ok = qi < pr.s_pad;
+  const int qc = row_ok ? qi : pr.s_pad - 1;
+  const int s_pad = pr.s_pad, s_valid = pr.s_valid, causal = pr.causal;
+
+  // this lane's allowed keys [lo, hi]
+  const DocBounds db = doc_bounds(pr.cu, pr.n_docs, qc, s_pad);
+  const int lo = db.lo;
+  const int hi = causal ? min(qc, s_valid - 1) : min(db.hi, s_valid) - 1;
+  // workgroup key range and the range that needs no mask
+  const DocBounds dfirst = doc_bounds(pr.cu, pr.n_docs, q0, s_pad);
+  const DocBounds dlast = doc_bounds(pr.cu, pr.n_docs, q1 - 1, s_pad);
+  const int kmin = dfirst.lo;
+  const int kmax = causal ? min(q1 - 1, s_valid - 1) : min(dlast.hi, s_valid) - 1;
+  const int free_lo = dlast.lo;
+  const int free_hi = causal ? min(q0, s_valid - 1) : min(dfirst.hi, s_valid) - 1;
+  // this wave's key range (waves of one workgroup may cover different rows)
+  const int wlast = min(wq0 + 31, s_pad - 1);
+  const int wkmin = doc_bounds(pr.cu, pr.n_docs, min(wq0, s_pad - 1), s_pad).lo;
+  const int wkmax = causal ? min(wlast, s_valid - 1)
+                           : min(doc_bounds(pr.cu, pr.n_docs, wlast, s_pad).hi, s_valid) - 1;
+
+  // Q fragment: B operand of S^T = K Q^T, lane holds Q[qc][16kk + 8hl .. +7]
+  bf16x8 qreg[8];
+  {
+    const __bf16* qp = pr.q + ((int64_t)qc * pr.hq + head) * D + hl * 8;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
+  }
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int tstart = (kmin / BN) * BN;
+  const int nt = kmax >= kmin ? (kmax - tstart) / BN + 1 : 0;
+
+  // staging: 4 K chunks + 4 V^T chunks of 16 bytes per thread
+  u32x4 stk[4], stv[4];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = (tid >> 4) + 16 * u, c = tid & 15;
+      const int j = t0 + r;
+      stk[u] = j < s_pad ? *reinterpret_cast<const u32x4*>(pr.k + ((int64_t)j * pr.hkv + kvh) * D + c * 8)
+                         : u32x4{0u, 0u, 0u, 0u};
+      const int dr = (tid >> 3) + 32 * u, c8 = tid & 7;
+      stv[u] = *reinterpret_cast<const u32x4*>(pr.vt + ((int64_t)kvh * D + dr) * pr.s_t + t0 + c8 * 8);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = (tid >> 4) + 16 * u, c = tid & 15;
+      *reinterpret_cast<u32x4*>(&lds_k[buf][r * KP + c * 8]) = stk[u];
+      const int dr = (tid >> 3) + 32 * u, c8 = tid & 7;
+      *reinterpret_cast<u32x4*>(&lds_v[buf][dr * VP + c8 * 8]) = stv[u];
+    }
+  };
+
+  if (nt > 0) {
+    load_tile(tstart);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < nt; ++it) {
+    const int t0 = tstart + it * BN;
+    const int buf = it & 1;
+    if (it + 1 < nt) load_tile(t0 + BN);
+
+    if (t0 <= wkmax && t0 + BN - 1 >= wkmin) {
+      // S^T = K Q^T for two 32-key blocks
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const __bf16* kp = &lds_k[buf][(kb * 32 + ln) * KP + hl * 8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+          sacc[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kp + kk * 16), qreg[kk], sacc[kb]);
+      }
+      const bool full = t0 >= free_lo && t0 + BN - 1 <= free_hi;
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = t0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+            if (key < lo || key > hi) sacc[kb][i] = -INFINITY;
+          }
+      }
+      // row max of this tile (raw scores), across both half-waves
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[0][i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[1][i]);
+      mx = half_swap_max(mx) * pr.scale_log2;
+      const bool need = mx > m_run + kRescaleThreshold;
+      if (__ballot(need)) {
+        const float mnew = need ? mx : m_run;
+        const float alpha = need ? exp2f(m_run - mnew) : 1.f;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
+        l_run *= alpha;
+        m_run = mnew;
+      }
+      const float msub = m_run == -INFINITY ? 0.f : m_run;
+      bf16x8 pb[4];
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          u32x4 pk;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * c + 2 * t], pr.scale_log2, -msub));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * c + 2 * t + 1], pr.scale_log2, -msub));
+            lsum += p0 + p1;
+            pk[t] = pack_bf16x2(p0, p1);
+          }
+          pb[kb * 2 + c] = __builtin_bit_cast(bf16x8, pk);
+        }
+      }
+      l_run += lsum;
+      // O^T += V^T P^T
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const __bf16* vp = &lds_v[buf][(b * 32 + ln) * VP + hl * 8];
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch)
+          oacc[b] = mfma32(*reinterpret_cast<const bf16x8*>(vp + ch * 16), pb[ch], oacc[b]);
+      }
+    }
+
+    if (it + 1 < nt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float l_tot = half_swap_sum(l_run);
+  if (row_ok) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    __bf16* op = pr.o + ((int64_t)qi * pr.hq + head) * D + hl * 4;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        u32x2 v2 = {pack_bf16x2(oacc[b][4 * r] * inv, oacc[b][4 * r + 1] * inv),
+                    pack_bf16x2(oacc[b][4 * r + 2] * inv, oacc[b][4 * r + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + b * 32 + r * 8) = v2;
+      }
+    if (hl == 0)
+      pr.lse[(int64_t)head * s_pad + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int HG>
+int launch_fwd(const FwdParams& p, int g, int hkv, hipStream_t stream) {
+  constexpr int QROWS = 32 * (4 / HG);
+  FwdParams pr = p;
+  pr.n_qblocks = (p.s_pad + QROWS - 1) / QROWS;
+  dim3 grid((unsigned)pr.n_qblocks, (unsigned)(hkv * (g / HG)));
+  TraceScope ts("attn_fwd_bf16", stream);
+  hipLaunchKernelGGL((fwd_bf16_kernel<HG>), grid, dim3(256), 0, stream, pr);
+  return hipGetLastError() == hipSuccess ? USP_OK : USP_ERR_HIP;
+}
+
+}  // namespace
+
+size_t attn_fwd_bf16_workspace(int64_t s_pad, int, int hkv, int d) {
+  return (size_t)hkv * d * kmajor_len(s_pad) * 2;
+}
+
+int attn_fwd_bf16(const AttnArgs& a) {
+  const int64_t s_t = kmajor_len(a.s_pad);
+  int rc = kmajor_launch(a.v, a.workspace, a.s_pad, a.hkv, s_t, a.stream, "attn_fwd_kmajor_v");
+  if (rc != USP_OK) return rc;
+  FwdParams p{};
+  p.q = static_cast<const __bf16*>(a.q);
+  p.k = static_cast<const __bf16*>(a.k);
+  p.vt = static_cast<const __bf16*>(a.workspace);
+  p.o = static_cast<__bf16*>(a.o_out);
+  p.lse = a.lse_out;
+  p.cu = a.cu;
+  p.s_t = s_t;
+  p.s_pad = (int)a.s_pad;
+  p.s_valid = (int)a.s_valid;
+  p.n_docs = a.n_docs;
+  p.hq = a.hq;
+  p.hkv = a.hkv;
+  p.causal = a.causal;
+  p.scale_log2 = a.scale * kLog2e;
+  const int g = a.hq / a.hkv;
+  if (g % 4 == 0) return launch_fwd<4>(p, g, a.hkv, a.stream);
+  if (g % 2 == 0) return launch_fwd<2>(p, g, a.hkv, a.stream);
+  return launch_fwd<1>(p, g, a.hkv, a.stream);
+}
+
+}  // namespace usp

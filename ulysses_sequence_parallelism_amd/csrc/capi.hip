@@ -1,0 +1,194 @@
+// C ABI entry points of libusp: host-side argument checks, then kernel
+// dispatch. Every check runs before the first HIP call, so a rejected call
+// enqueues nothing and touches no device state (and can be exercised on a
+// machine without a GPU).
+#include <math.h>
+
+#include "usp_common.h"
+#include "usp_internal.h"
+
+namespace {
+
+constexpr int kAbiVersion = 100;
+
+size_t elem_bytes(int dtype) { return dtype == USP_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+bool overlap(Span a, Span b) {
+  if (a.p == nullptr || b.p == nullptr || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+int check_permute(const void* src, const void* dst, int64_t s_real, int p, int h, int d,
+                  int dtype, size_t* src_bytes, size_t* dst_bytes, int64_t* s_pad) {
+  if (dtype != USP_BF16 && dtype != USP_FP32) return USP_ERR_UNSUPPORTED;
+  if (p < 1 || h < 1 || d < 1 || s_real < 0) return USP_ERR_INVALID;
+  if (h % p != 0) return USP_ERR_INVALID;  // head count must divide the Ulysses degree
+  const int64_t es = (int64_t)elem_bytes(dtype);
+  const int64_t row_bytes = (int64_t)h * d * es;
+  if ((row_bytes / p) % 4 != 0) return USP_ERR_UNSUPPORTED;
+  *s_pad = usp_padded_len(s_real, p);
+  // kernels index 4-byte chunks with 32-bit integers
+  if (*s_pad > 0 && (double)(*s_pad) * (double)(row_bytes / 4) >= 2147483648.0) return USP_ERR_INVALID;
+  *src_bytes = (size_t)(s_real * row_bytes);
+  *dst_bytes = (size_t)(*s_pad * row_bytes);
+  return USP_OK;
+}
+
+int check_attn(int64_t s_pad, int64_t s_valid, const int32_t* cu, int n_docs, int hq, int hkv,
+               int d, float scale, int causal, int dtype) {
+  if (dtype != USP_BF16 && dtype != USP_FP32) return USP_ERR_UNSUPPORTED;
+  if (s_pad < 1 || s_pad >= (int64_t)1 << 30) return USP_ERR_INVALID;
+  if (s_valid < 1 || s_valid > s_pad) return USP_ERR_INVALID;
+  if (hq < 1 || hkv < 1 || hq % hkv != 0) return USP_ERR_INVALID;
+  if (!(scale > 0.f) || !isfinite(scale)) return USP_ERR_INVALID;
+  if (causal != 0 && causal != 1) return USP_ERR_INVALID;
+  if (cu != nullptr && (n_docs < 1 || s_valid != s_pad)) return USP_ERR_INVALID;
+  if (dtype == USP_BF16 && d != 128) return USP_ERR_UNSUPPORTED;
+  if (dtype == USP_FP32 && d != 64 && d != 128) return USP_ERR_UNSUPPORTED;
+  if ((double)s_pad * hq * d >= 9.0e15) return USP_ERR_INVALID;
+  return USP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int usp_version(void) { return kAbiVersion; }
+
+const char* usp_status_string(int status) {
+  switch (status) {
+    case USP_OK: return "ok";
+    case USP_ERR_INVALID: return "invalid argument (shape, divisibility, range, alignment or aliasing)";
+    case USP_ERR_UNSUPPORTED: return "unsupported dtype or head dimension";
+    case USP_ERR_NULL: return "required pointer is NULL";
+    case USP_ERR_HIP: return "HIP runtime error while launching";
+    case USP_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int64_t usp_padded_len(int64_t s_real, int p) {
+  if (p < 1 || s_real < 0) return -1;
+  return (s_real + p - 1) / p * p;
+}
+
+static int permute_entry(bool pack, const void* src, void* dst, int64_t s_real, int p, int h,
+                         int d, int dtype, void* stream) {
+  size_t src_bytes = 0, dst_bytes = 0;
+  int64_t s_pad = 0;
+  const int64_t s_rows = s_real;
+  // for the pack src is x [s_real][h][d]; for the unpack src is y [p][s_pad][h/p][d]
+  int rc = check_permute(src, dst, s_rows, p, h, d, dtype, &src_bytes, &dst_bytes, &s_pad);
+  if (rc != USP_OK) return rc;
+  const size_t x_bytes = src_bytes, y_bytes = dst_bytes;
+  const size_t in_bytes = pack ? x_bytes : y_bytes;
+  const size_t out_bytes = pack ? y_bytes : x_bytes;
+  if (out_bytes == 0) return USP_OK;
+  if ((in_bytes > 0 && src == nullptr) || dst == nullptr) return USP_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst)) return USP_ERR_INVALID;
+  if (overlap({src, in_bytes}, {dst, out_bytes})) return USP_ERR_INVALID;
+  const int64_t row_bytes = (int64_t)h * d * (int64_t)elem_bytes(dtype);
+  return usp::permute_launch(pack, src, dst, s_real, s_pad, p, row_bytes,
+                             static_cast<hipStream_t>(stream));
+}
+
+int usp_pad_pack_seq2head(const void* x, void* y, int64_t s_real, int p, int h, int d, int dtype,
+                          void* stream) {
+  return permute_entry(true, x, y, s_real, p, h, d, dtype, stream);
+}
+
+int usp_unpack_head2seq(const void* y, void* x, int64_t s_real, int p, int h, int d, int dtype,
+                        void* stream) {
+  return permute_entry(false, y, x, s_real, p, h, d, dtype, stream);
+}
+
+size_t usp_attn_fwd_workspace_bytes(int64_t s_pad, int hq, int hkv, int d, int dtype) {
+  if (s_pad < 1 || hq < 1 || hkv < 1 || d < 1) return 0;
+  if (dtype == USP_BF16) return usp::attn_fwd_bf16_workspace(s_pad, hq, hkv, d);
+  return 0;
+}
+
+size_t usp_attn_bwd_workspace_bytes(int64_t s_pad, int hq, int hkv, int d, int dtype) {
+  if (s_pad < 1 || hq < 1 || hkv < 1 || d < 1) return 0;
+  if (dtype == USP_BF16) return usp::attn_bwd_bf16_workspace(s_pad, hq, hkv, d);
+  return usp::attn_bwd_f32_workspace(s_pad, hq, hkv, d);
+}
+
+int usp_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 void* workspace, size_t workspace_bytes, int64_t s_pad, int64_t s_valid,
+                 const int32_t* cu_seqlens, int n_docs, int hq, int hkv, int d,
+                 float softmax_scale, int causal, int dtype, void* stream) {
+  int rc = check_attn(s_pad, s_valid, cu_seqlens, n_docs, hq, hkv, d, softmax_scale, causal, dtype);
+  if (rc != USP_OK) return rc;
+  if (!q || !k || !v || !o || !lse) return USP_ERR_NULL;
+  const void* ptrs[] = {q, k, v, o, lse};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return USP_ERR_INVALID;
+  if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return USP_ERR_INVALID;
+  const size_t es = elem_bytes(dtype);
+  const size_t qb = (size_t)s_pad * hq * d * es, kb = (size_t)s_pad * hkv * d * es;
+  const size_t lb = (size_t)s_pad * hq * sizeof(float);
+  const size_t need = usp_attn_fwd_workspace_bytes(s_pad, hq, hkv, d, dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return USP_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return USP_ERR_INVALID;
+  const Span ins[] = {{q, qb}, {k, kb}, {v, kb}};
+  const Span outs[] = {{o, qb}, {lse, lb}, {workspace, need}};
+  for (const Span& a : outs) {
+    for (const Span& b : ins)
+      if (overlap(a, b)) return USP_ERR_INVALID;
+  }
+  if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2]))
+    return USP_ERR_INVALID;
+  usp::AttnArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.o_out = o; a.lse_out = lse; a.workspace = workspace;
+  a.s_pad = s_pad; a.s_valid = s_valid; a.cu = cu_seqlens; a.n_docs = n_docs;
+  a.hq = hq; a.hkv = hkv; a.d = d; a.scale = softmax_scale; a.causal = causal;
+  a.stream = static_cast<hipStream_t>(stream);
+  return dtype == USP_BF16 ? usp::attn_fwd_bf16(a) : usp::attn_fwd_f32(a);
+}
+
+int usp_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, int64_t s_pad, int64_t s_valid,
+                 const int32_t* cu_seqlens, int n_docs, int hq, int hkv, int d,
+                 float softmax_scale, int causal, int dtype, void* stream) {
+  int rc = check_attn(s_pad, s_valid, cu_seqlens, n_docs, hq, hkv, d, softmax_scale, causal, dtype);
+  if (rc != USP_OK) return rc;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return USP_ERR_NULL;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return USP_ERR_INVALID;
+  if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return USP_ERR_INVALID;
+  const size_t es = elem_bytes(dtype);
+  const size_t qb = (size_t)s_pad * hq * d * es, kb = (size_t)s_pad * hkv * d * es;
+  const size_t lb = (size_t)s_pad * hq * sizeof(float);
+  const size_t need = usp_attn_bwd_workspace_bytes(s_pad, hq, hkv, d, dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return USP_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return USP_ERR_INVALID;
+  const Span ins[] = {{q, qb}, {k, kb}, {v, kb}, {o, qb}, {lse, lb}, {dout, qb}};
+  const Span outs[] = {{dq, qb}, {dk, kb}, {dv, kb}, {workspace, need}};
+  for (const Span& a : outs)
+    for (const Span& b : ins)
+      if (overlap(a, b)) return USP_ERR_INVALID;
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return USP_ERR_INVALID;
+  usp::AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.workspace = workspace;
+  a.s_pad = s_pad; a.s_valid = s_valid; a.cu = cu_seqlens; a.n_docs = n_docs;
+  a.hq = hq; a.hkv = hkv; a.d = d; a.scale = softmax_scale; a.causal = causal;
+  a.stream = static_cast<hipStream_t>(stream);
+  return dtype == USP_BF16 ? usp::attn_bwd_bf16(a) : usp::attn_bwd_f32(a);
+}
+
+}  // extern "C"
