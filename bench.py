@@ -40,7 +40,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="s120k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=12000)
+    ap.add_argument("--cpu-sample-rows", type=int, default=24000)
+    ap.add_argument("--counters", action="store_true",
+                    help="for rocprofv3 --pmc runs: one warm-up step, one step, then a plain "
+                         "1 GiB device copy that calibrates the byte counters; no JSON line")
     return ap.parse_args()
 
 
@@ -178,6 +181,19 @@ def main():
         usp.usp_attn_bwd(q, k, v, o, lse, do, s_valid=w.s, dq=dq, dk=dk, dv=dv, workspace=ws_b)
         for n, a in (("dq", dq), ("dk", dk), ("dv", dv)):
             usp.usp_unpack_head2seq(a.view(p, s_loc, a.shape[1], d), s_loc, out=back[n])
+
+    if args.counters:
+        step()
+        torch.cuda.synchronize()
+        step()
+        torch.cuda.synchronize()
+        a = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)  # calibration: reads and writes exactly 1 GiB
+        torch.cuda.synchronize()
+        print("counters run done", flush=True)
+        return
 
     for _ in range(args.warmup):
         step()

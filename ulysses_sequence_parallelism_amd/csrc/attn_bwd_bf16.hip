@@ -28,13 +28,19 @@
 #include "usp_common.h"
 #include "usp_internal.h"
 
+#ifndef DQ_KEYS
+#define DQ_KEYS 32
+#endif
+#ifndef DKDV_ROWS
+#define DKDV_ROWS 64
+#endif
+
 namespace usp {
 
 namespace {
 
 constexpr int D = 128;
 constexpr int KP = D + 8;    // row-major tile pitch (elements)
-constexpr int TP = 64 + 8;   // key-major tile pitch (elements)
 
 // ---------------------------------------------------------------------------
 // D_i = sum_d dO[i][h][d] * O[i][h][d]  (fp32 from the bf16 values)
@@ -84,25 +90,39 @@ struct BwdParams {
 };
 
 // ---------------------------------------------------------------------------
-// dK / dV: key-stationary. Workgroup = 4 waves x 32 keys of one KV head.
-constexpr int BQ = 64;  // query rows per tile
-
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams pr) {
+// dK / dV: key-stationary. A workgroup owns 128 keys of one KV head (four
+// groups of 32) and walks every query tile (BQ rows) of every query head of
+// the group that can see them. Each key group is served by a PAIR of waves:
+//   role 0: S = Q K^T -> P -> dV^T += dO^T P   (K fragments stationary)
+//   role 1: dP = dO V^T -> dS = P (dP - D) -> dK^T += Q^T dS   (V stationary)
+// P crosses from role 0 to role 1 through LDS in accumulator register order
+// (16 bytes per lane per 16-row chunk, conflict-free). Splitting the work
+// halves each wave's live state (one stationary operand, one accumulator), so
+// two waves fit per SIMD and one wave's MFMAs overlap the other's softmax and
+// LDS traffic.
+template <int BQ>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
+  constexpr int MB = BQ / 32;          // 32-row blocks per tile
+  constexpr int NCH = 2 * MB;          // 16-row chunks per tile
+  constexpr int TQ = BQ + 8;           // key-major tile pitch (elements)
+  constexpr int RCH = BQ / 32;         // 16-byte chunks per thread per tile
   __shared__ __attribute__((aligned(16))) __bf16 lq[2][BQ * KP];
   __shared__ __attribute__((aligned(16))) __bf16 ldo[2][BQ * KP];
-  __shared__ __attribute__((aligned(16))) __bf16 lqt[2][D * TP];
-  __shared__ __attribute__((aligned(16))) __bf16 ldot[2][D * TP];
+  __shared__ __attribute__((aligned(16))) __bf16 lqt[2][D * TQ];
+  __shared__ __attribute__((aligned(16))) __bf16 ldot[2][D * TQ];
   __shared__ __attribute__((aligned(16))) float llse[2][BQ];
   __shared__ __attribute__((aligned(16))) float ldd[2][BQ];
+  __shared__ __attribute__((aligned(16))) u32x4 lp[4][NCH][64];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int grp = w & 3, role = w >> 2;
   const int hl = lane >> 5, ln = lane & 31;
   const int s_pad = pr.s_pad, s_valid = pr.s_valid, causal = pr.causal;
   const int g = pr.hq / pr.hkv;
   const int kvh = blockIdx.y;
   const int j0 = blockIdx.x * 128;
   const int j1 = min(j0 + 128, s_pad);
-  const int wj0 = j0 + w * 32;
+  const int wj0 = j0 + grp * 32;
   const int key = wj0 + ln;
   const int kc = min(key, s_pad - 1);
 
@@ -119,70 +139,73 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams pr) {
   const int free_lo = max(dlast.lo, causal ? j1 - 1 : 0);
   const int free_hi = dfirst.hi - 1;
   const bool all_keys_valid = j1 - 1 < s_valid;
-  // this wave's row range
+  // this key group's row range
   const int wlast = min(wj0 + 31, s_pad - 1);
   const bool wave_live = wj0 < s_pad && wj0 < s_valid;
   const int wr_lo = causal ? wj0 : doc_bounds(pr.cu, pr.n_docs, min(wj0, s_pad - 1), s_pad).lo;
   const int wr_hi = doc_bounds(pr.cu, pr.n_docs, wlast, s_pad).hi - 1;
 
-  // stationary K and V fragments (B operands), lane = key
-  bf16x8 kreg[8], vreg[8];
+  // stationary fragment (B operand, lane = key): K for role 0, V for role 1
+  bf16x8 sreg[8];
   {
+    const __bf16* src = role == 0 ? pr.k : pr.v;
     const int64_t off = ((int64_t)kc * pr.hkv + kvh) * D + hl * 8;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      kreg[kk] = *reinterpret_cast<const bf16x8*>(pr.k + off + kk * 16);
-      vreg[kk] = *reinterpret_cast<const bf16x8*>(pr.v + off + kk * 16);
-    }
+    for (int kk = 0; kk < 8; ++kk) sreg[kk] = *reinterpret_cast<const bf16x8*>(src + off + kk * 16);
   }
-  f32x16 dka[4], dva[4];
+  // Retire the stationary loads here; otherwise the wait-count pass treats
+  // them as possibly in flight inside the loop and makes every MFMA wait for
+  // the next tile's loads too.
+  __builtin_amdgcn_s_waitcnt(0);
+  f32x16 acc[4];  // dV^T (role 0) or dK^T (role 1): rows = d, cols = keys
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    dka[b] = f32x16{};
-    dva[b] = f32x16{};
-  }
+  for (int b = 0; b < 4; ++b) acc[b] = f32x16{};
 
   const int tstart = (rstart / BQ) * BQ;
   const int ntr = (j0 < s_valid && rend >= rstart) ? (rend - tstart) / BQ + 1 : 0;
   const int nt = ntr * g;
 
-  u32x4 sq[4], sdo[4], sqt[4], sdot[4];
-  float slse = 0.f, sdd = 0.f;
+  u32x4 sq[RCH], sdo[RCH], sqt[RCH], sdot[RCH];
+  float sld = 0.f;
   auto load_tile = [&](int it) {
     const int h = kvh * g + it / ntr;
     const int r0 = tstart + (it % ntr) * BQ;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = (tid >> 4) + 16 * u, c = tid & 15;
-      const int i = r0 + r;
+    for (int u = 0; u < RCH; ++u) {
+      const int e = tid + 512 * u;
+      const int r = e >> 4, c = e & 15;
+      // rows past the end read the last row instead: every load is
+      // unconditional (no wait is forced before the tile is consumed) and
+      // such rows are always masked
+      const int i = min(r0 + r, s_pad - 1);
       const int64_t off = ((int64_t)i * pr.hq + h) * D + c * 8;
-      sq[u] = i < s_pad ? *reinterpret_cast<const u32x4*>(pr.q + off) : u32x4{0u, 0u, 0u, 0u};
-      sdo[u] = i < s_pad ? *reinterpret_cast<const u32x4*>(pr.dout + off) : u32x4{0u, 0u, 0u, 0u};
-      const int dr = (tid >> 3) + 32 * u, c8 = tid & 7;
+      sq[u] = *reinterpret_cast<const u32x4*>(pr.q + off);
+      sdo[u] = *reinterpret_cast<const u32x4*>(pr.dout + off);
+      const int dr = e / (BQ / 8), c8 = e % (BQ / 8);
       const int64_t toff = ((int64_t)h * D + dr) * pr.s_t + r0 + c8 * 8;
       sqt[u] = *reinterpret_cast<const u32x4*>(pr.qt + toff);
       sdot[u] = *reinterpret_cast<const u32x4*>(pr.dot + toff);
     }
-    if (tid < BQ) {
-      const int i = r0 + tid;
-      slse = i < s_pad ? pr.lse[(int64_t)h * s_pad + i] * kLog2e : 0.f;
-      sdd = i < s_pad ? pr.dd[(int64_t)h * pr.s_t + i] : 0.f;
+    {
+      // threads [0, BQ) fetch LSE, [BQ, 2 BQ) fetch D, the rest a dummy
+      const int i = min(r0 + (tid % BQ), s_pad - 1);
+      const float* src = tid < BQ ? pr.lse + (int64_t)h * s_pad : pr.dd + (int64_t)h * pr.s_t;
+      sld = src[i];
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = (tid >> 4) + 16 * u, c = tid & 15;
+    for (int u = 0; u < RCH; ++u) {
+      const int e = tid + 512 * u;
+      const int r = e >> 4, c = e & 15;
       *reinterpret_cast<u32x4*>(&lq[buf][r * KP + c * 8]) = sq[u];
       *reinterpret_cast<u32x4*>(&ldo[buf][r * KP + c * 8]) = sdo[u];
-      const int dr = (tid >> 3) + 32 * u, c8 = tid & 7;
-      *reinterpret_cast<u32x4*>(&lqt[buf][dr * TP + c8 * 8]) = sqt[u];
-      *reinterpret_cast<u32x4*>(&ldot[buf][dr * TP + c8 * 8]) = sdot[u];
+      const int dr = e / (BQ / 8), c8 = e % (BQ / 8);
+      *reinterpret_cast<u32x4*>(&lqt[buf][dr * TQ + c8 * 8]) = sqt[u];
+      *reinterpret_cast<u32x4*>(&ldot[buf][dr * TQ + c8 * 8]) = sdot[u];
     }
-    if (tid < BQ) {
-      llse[buf][tid] = slse;
-      ldd[buf][tid] = sdd;
-    }
+    if (tid < BQ) llse[buf][tid] = sld * kLog2e;
+    else if (tid < 2 * BQ) ldd[buf][tid - BQ] = sld;
   };
 
   if (nt > 0) {
@@ -195,63 +218,85 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams pr) {
     const int buf = it & 1;
     const int r0 = tstart + (it % ntr) * BQ;
     if (it + 1 < nt) load_tile(it + 1);
+    const bool active = wave_live && r0 + BQ - 1 >= wr_lo && r0 <= wr_hi;
 
-    if (wave_live && r0 + BQ - 1 >= wr_lo && r0 <= wr_hi) {
-      // S = Q K^T and dP = dO V^T: rows = queries (two 32-row blocks), cols = keys
-      f32x16 sa[2] = {f32x16{}, f32x16{}}, pa[2] = {f32x16{}, f32x16{}};
+    // phase 1: role 0 -> P (to LDS and registers); role 1 -> dP (registers)
+    f32x16 pa[MB];
+    bf16x8 pb[NCH];
+    if (active) {
+      const __bf16* base = role == 0 ? lq[buf] : ldo[buf];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const __bf16* qp = &lq[buf][(mb * 32 + ln) * KP + hl * 8];
-        const __bf16* dp = &ldo[buf][(mb * 32 + ln) * KP + hl * 8];
+      for (int mb = 0; mb < MB; ++mb) {
+        pa[mb] = f32x16{};
+        const __bf16* ap = base + (mb * 32 + ln) * KP + hl * 8;
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          sa[mb] = mfma32(*reinterpret_cast<const bf16x8*>(qp + kk * 16), kreg[kk], sa[mb]);
-          pa[mb] = mfma32(*reinterpret_cast<const bf16x8*>(dp + kk * 16), vreg[kk], pa[mb]);
-        }
+        for (int kk = 0; kk < 8; ++kk)
+          pa[mb] = mfma32(*reinterpret_cast<const bf16x8*>(ap + kk * 16), sreg[kk], pa[mb]);
       }
-      const bool full = all_keys_valid && r0 >= free_lo && r0 + BQ - 1 <= free_hi;
-      bf16x8 pt[4], dst[4];
+      if (role == 0) {
+        // rows [mlo, mhi) keep their probability; a mask-free tile uses a
+        // range that contains every row of the tile
+        const bool full = all_keys_valid && r0 >= free_lo && r0 + BQ - 1 <= free_hi;
+        const int mlo = full ? r0 : (key_ok ? rlo : s_pad);
+        const int mhi = full ? r0 + BQ : (key_ok ? rhi : 0);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int rr = mb * 32 + r4 * 8 + hl * 4;  // first of 4 consecutive rows
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&llse[buf][rr]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&ldd[buf][rr]);
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int rr = mb * 32 + r4 * 8 + hl * 4;  // first of 4 consecutive rows
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&llse[buf][rr]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = r4 * 4 + e;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[mb][i], pr.scale_log2, -l4[e]));
-            if (!full) {
+            for (int e = 0; e < 4; ++e) {
+              const int i = r4 * 4 + e;
+              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(pa[mb][i], pr.scale_log2, -l4[e]));
               const int row = r0 + rr + e;
-              if (!(key_ok && row >= rlo && row < rhi)) p = 0.f;
+              pa[mb][i] = (row >= mlo && row < mhi) ? p : 0.f;
             }
-            sa[mb][i] = p;
-            pa[mb][i] = p * (pa[mb][i] - d4[e]);
           }
-        }
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          u32x4 a, b;
+          for (int c = 0; c < 2; ++c) {
+            u32x4 a;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            a[t] = pack_bf16x2(sa[mb][8 * c + 2 * t], sa[mb][8 * c + 2 * t + 1]);
-            b[t] = pack_bf16x2(pa[mb][8 * c + 2 * t], pa[mb][8 * c + 2 * t + 1]);
+            for (int t = 0; t < 4; ++t) a[t] = pack_bf16x2(pa[mb][8 * c + 2 * t], pa[mb][8 * c + 2 * t + 1]);
+            pb[mb * 2 + c] = __builtin_bit_cast(bf16x8, a);
+            lp[grp][mb * 2 + c][lane] = a;
           }
-          pt[mb * 2 + c] = __builtin_bit_cast(bf16x8, a);
-          dst[mb * 2 + c] = __builtin_bit_cast(bf16x8, b);
         }
       }
-      // dV^T += dO^T P,  dK^T += Q^T dS  (rows = d, cols = keys)
+    }
+    __syncthreads();  // P is visible to role 1
+
+    // phase 2: role 0 -> dV^T += dO^T P; role 1 -> dS, dK^T += Q^T dS
+    if (active) {
+      if (role == 1) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const u32x4 praw = lp[grp][mb * 2 + c][lane];
+            const bf16x8 pv = __builtin_bit_cast(bf16x8, praw);
+            const f32x4 d4a = *reinterpret_cast<const f32x4*>(&ldd[buf][mb * 32 + (2 * c) * 8 + hl * 4]);
+            const f32x4 d4b = *reinterpret_cast<const f32x4*>(&ldd[buf][mb * 32 + (2 * c + 1) * 8 + hl * 4]);
+            u32x4 o;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int i0 = 8 * c + 2 * t, i1 = i0 + 1;  // accumulator registers
+              const float dd0 = (i0 >> 2) == 2 * c ? d4a[i0 & 3] : d4b[i0 & 3];
+              const float dd1 = (i1 >> 2) == 2 * c ? d4a[i1 & 3] : d4b[i1 & 3];
+              const float p0 = (float)pv[2 * t], p1 = (float)pv[2 * t + 1];
+              o[t] = pack_bf16x2(p0 * (pa[mb][i0] - dd0), p1 * (pa[mb][i1] - dd1));
+            }
+            pb[mb * 2 + c] = __builtin_bit_cast(bf16x8, o);
+          }
+        }
+      }
+      const __bf16* tbase = role == 0 ? ldot[buf] : lqt[buf];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const __bf16* op = &ldot[buf][(b * 32 + ln) * TP + hl * 8];
-        const __bf16* qp = &lqt[buf][(b * 32 + ln) * TP + hl * 8];
+        const __bf16* tp = tbase + (b * 32 + ln) * TQ + hl * 8;
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch) {
-          dva[b] = mfma32(*reinterpret_cast<const bf16x8*>(op + ch * 16), pt[ch], dva[b]);
-          dka[b] = mfma32(*reinterpret_cast<const bf16x8*>(qp + ch * 16), dst[ch], dka[b]);
-        }
+        for (int ch = 0; ch < NCH; ++ch)
+          acc[b] = mfma32(*reinterpret_cast<const bf16x8*>(tp + ch * 16), pb[ch], acc[b]);
       }
     }
     if (it + 1 < nt) store_tile(buf ^ 1);
@@ -259,33 +304,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams pr) {
   }
 
   if (key < s_pad) {
-    __bf16* kp = pr.dk + ((int64_t)key * pr.hkv + kvh) * D + hl * 4;
-    __bf16* vp = pr.dv + ((int64_t)key * pr.hkv + kvh) * D + hl * 4;
+    const float f = role == 0 ? 1.f : pr.scale;
+    __bf16* op = (role == 0 ? pr.dv : pr.dk) + ((int64_t)key * pr.hkv + kvh) * D + hl * 4;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        u32x2 k2 = {pack_bf16x2(dka[b][4 * r] * pr.scale, dka[b][4 * r + 1] * pr.scale),
-                    pack_bf16x2(dka[b][4 * r + 2] * pr.scale, dka[b][4 * r + 3] * pr.scale)};
-        u32x2 v2 = {pack_bf16x2(dva[b][4 * r], dva[b][4 * r + 1]),
-                    pack_bf16x2(dva[b][4 * r + 2], dva[b][4 * r + 3])};
-        *reinterpret_cast<u32x2*>(kp + b * 32 + r * 8) = k2;
-        *reinterpret_cast<u32x2*>(vp + b * 32 + r * 8) = v2;
+        u32x2 v2 = {pack_bf16x2(acc[b][4 * r] * f, acc[b][4 * r + 1] * f),
+                    pack_bf16x2(acc[b][4 * r + 2] * f, acc[b][4 * r + 3] * f)};
+        *reinterpret_cast<u32x2*>(op + b * 32 + r * 8) = v2;
       }
   }
 }
 
 // ---------------------------------------------------------------------------
 // dQ: query-stationary. Workgroup = 4 waves sharing one KV head (HG heads x
-// 4/HG blocks of 32 query rows), as in the forward.
-constexpr int BN = 64;  // keys per tile
-
-template <int HG>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams pr) {
+// 4/HG blocks of 32 query rows), as in the forward; keys are walked in tiles of
+// BN (BN / 32 MFMA key blocks). With BN = 32 two workgroups fit per CU.
+template <int HG, int BN>
+__global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdParams pr) {
   constexpr int QROWS = 32 * (4 / HG);
+  constexpr int KB = BN / 32;
+  constexpr int TK = BN + 8;
+  constexpr int RCH = BN / 16;
   __shared__ __attribute__((aligned(16))) __bf16 lk[2][BN * KP];
   __shared__ __attribute__((aligned(16))) __bf16 lv[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) __bf16 lkt[2][D * TP];
+  __shared__ __attribute__((aligned(16))) __bf16 lkt[2][D * TK];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hl = lane >> 5, ln = lane & 31;
@@ -327,6 +371,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams pr) {
   }
   const float lse2 = pr.lse[(int64_t)head * s_pad + qc] * kLog2e;
   const float drow = pr.dd[(int64_t)head * pr.s_t + qc];
+  // retire the stationary loads before the loop (see the dK/dV kernel)
+  __builtin_amdgcn_s_waitcnt(0);
 
   f32x16 dqa[4];
 #pragma unroll
@@ -335,27 +381,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams pr) {
   const int tstart = (kmin / BN) * BN;
   const int nt = kmax >= kmin ? (kmax - tstart) / BN + 1 : 0;
 
-  u32x4 sk[4], sv[4], skt[4];
+  u32x4 sk[RCH], sv[RCH], skt[RCH];
   auto load_tile = [&](int t0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = (tid >> 4) + 16 * u, c = tid & 15;
-      const int j = t0 + r;
+    for (int u = 0; u < RCH; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e >> 4, c = e & 15;
+      // keys past the end read the last key (always masked): unconditional loads
+      const int j = min(t0 + r, s_pad - 1);
       const int64_t off = ((int64_t)j * pr.hkv + kvh) * D + c * 8;
-      sk[u] = j < s_pad ? *reinterpret_cast<const u32x4*>(pr.k + off) : u32x4{0u, 0u, 0u, 0u};
-      sv[u] = j < s_pad ? *reinterpret_cast<const u32x4*>(pr.v + off) : u32x4{0u, 0u, 0u, 0u};
-      const int dr = (tid >> 3) + 32 * u, c8 = tid & 7;
+      sk[u] = *reinterpret_cast<const u32x4*>(pr.k + off);
+      sv[u] = *reinterpret_cast<const u32x4*>(pr.v + off);
+      const int dr = e / (BN / 8), c8 = e % (BN / 8);
       skt[u] = *reinterpret_cast<const u32x4*>(pr.kt + ((int64_t)kvh * D + dr) * pr.s_t + t0 + c8 * 8);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = (tid >> 4) + 16 * u, c = tid & 15;
+    for (int u = 0; u < RCH; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e >> 4, c = e & 15;
       *reinterpret_cast<u32x4*>(&lk[buf][r * KP + c * 8]) = sk[u];
       *reinterpret_cast<u32x4*>(&lv[buf][r * KP + c * 8]) = sv[u];
-      const int dr = (tid >> 3) + 32 * u, c8 = tid & 7;
-      *reinterpret_cast<u32x4*>(&lkt[buf][dr * TP + c8 * 8]) = skt[u];
+      const int dr = e / (BN / 8), c8 = e % (BN / 8);
+      *reinterpret_cast<u32x4*>(&lkt[buf][dr * TK + c8 * 8]) = skt[u];
     }
   };
 
@@ -371,9 +420,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams pr) {
     if (it + 1 < nt) load_tile(t0 + BN);
 
     if (t0 <= wkmax && t0 + BN - 1 >= wkmin) {
-      f32x16 sa[2] = {f32x16{}, f32x16{}}, pa[2] = {f32x16{}, f32x16{}};
+      f32x16 sa[KB], pa[KB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
+        sa[kb] = f32x16{};
+        pa[kb] = f32x16{};
         const __bf16* kp = &lk[buf][(kb * 32 + ln) * KP + hl * 8];
         const __bf16* vp = &lv[buf][(kb * 32 + ln) * KP + hl * 8];
 #pragma unroll
@@ -383,16 +434,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams pr) {
         }
       }
       const bool full = t0 >= free_lo && t0 + BN - 1 <= free_hi;
-      bf16x8 dst[4];
+      const int mlo = full ? t0 : lo;
+      const int mhi = full ? t0 + BN - 1 : hi;
+      bf16x8 dst[2 * KB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[kb][i], pr.scale_log2, -lse2));
-          if (!full) {
-            const int key = t0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-            if (key < lo || key > hi) p = 0.f;
-          }
+          const int key = t0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+          p = (key >= mlo && key <= mhi) ? p : 0.f;
           pa[kb][i] = p * (pa[kb][i] - drow);
         }
 #pragma unroll
@@ -406,9 +457,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams pr) {
       // dQ^T += K^T dS^T (rows = d, cols = queries)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const __bf16* tp = &lkt[buf][(b * 32 + ln) * TP + hl * 8];
+        const __bf16* tp = &lkt[buf][(b * 32 + ln) * TK + hl * 8];
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch)
+        for (int ch = 0; ch < 2 * KB; ++ch)
           dqa[b] = mfma32(*reinterpret_cast<const bf16x8*>(tp + ch * 16), dst[ch], dqa[b]);
       }
     }
@@ -429,6 +480,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams pr) {
   }
 }
 
+constexpr int kDqKeys = DQ_KEYS;     // keys per dQ tile
+constexpr int kDkdvRows = DKDV_ROWS; // query rows per dK/dV tile
+
 template <int HG>
 int launch_dq(const BwdParams& p, int g, hipStream_t stream) {
   constexpr int QROWS = 32 * (4 / HG);
@@ -436,7 +490,7 @@ int launch_dq(const BwdParams& p, int g, hipStream_t stream) {
   pr.n_blocks = (p.s_pad + QROWS - 1) / QROWS;
   dim3 grid((unsigned)pr.n_blocks, (unsigned)(p.hkv * (g / HG)));
   TraceScope ts("attn_bwd_dq_bf16", stream);
-  hipLaunchKernelGGL((bwd_dq_kernel<HG>), grid, dim3(256), 0, stream, pr);
+  hipLaunchKernelGGL((bwd_dq_kernel<HG, kDqKeys>), grid, dim3(256), 0, stream, pr);
   return hipGetLastError() == hipSuccess ? USP_OK : USP_ERR_HIP;
 }
 
@@ -498,7 +552,7 @@ int attn_bwd_bf16(const AttnArgs& a) {
   {
     dim3 grid((unsigned)((a.s_pad + 127) / 128), (unsigned)a.hkv);
     TraceScope ts("attn_bwd_dkdv_bf16", a.stream);
-    hipLaunchKernelGGL(bwd_dkdv_kernel, grid, dim3(256), 0, a.stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<kDkdvRows>), grid, dim3(512), 0, a.stream, p);
     if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
   }
   const int g = a.hq / a.hkv;

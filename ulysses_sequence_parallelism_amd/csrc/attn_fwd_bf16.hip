@@ -106,6 +106,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams pr) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
   }
+  // Retire the Q loads here; otherwise the wait-count pass treats them as
+  // possibly in flight inside the loop and makes the MFMAs wait for the next
+  // tile's loads too.
+  __builtin_amdgcn_s_waitcnt(0);
 
   f32x16 oacc[4];
 #pragma unroll
@@ -121,9 +125,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams pr) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int r = (tid >> 4) + 16 * u, c = tid & 15;
-      const int j = t0 + r;
-      stk[u] = j < s_pad ? *reinterpret_cast<const u32x4*>(pr.k + ((int64_t)j * pr.hkv + kvh) * D + c * 8)
-                         : u32x4{0u, 0u, 0u, 0u};
+      // keys past the end read the last key (always masked): unconditional loads
+      const int j = min(t0 + r, s_pad - 1);
+      stk[u] = *reinterpret_cast<const u32x4*>(pr.k + ((int64_t)j * pr.hkv + kvh) * D + c * 8);
       const int dr = (tid >> 3) + 32 * u, c8 = tid & 7;
       stv[u] = *reinterpret_cast<const u32x4*>(pr.vt + ((int64_t)kvh * D + dr) * pr.s_t + t0 + c8 * 8);
     }
