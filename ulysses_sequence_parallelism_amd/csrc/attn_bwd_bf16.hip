@@ -167,9 +167,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
 
   u32x4 sq[RCH], sdo[RCH], sqt[RCH], sdot[RCH];
   float sld = 0.f;
+  // Tile order: query tiles from the END of the sequence downwards, the heads
+  // of the group innermost. Every resident workgroup then reads the same
+  // (row tile, head) at about the same time, whatever its key block, so the
+  // tiles are shared through L2 instead of each workgroup streaming its own
+  // row range.
+  auto tile_row = [&](int it) { return tstart + (ntr - 1 - it / g) * BQ; };
   auto load_tile = [&](int it) {
-    const int h = kvh * g + it / ntr;
-    const int r0 = tstart + (it % ntr) * BQ;
+    const int h = kvh * g + it % g;
+    const int r0 = tile_row(it);
 #pragma unroll
     for (int u = 0; u < RCH; ++u) {
       const int e = tid + 512 * u;
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
 
   for (int it = 0; it < nt; ++it) {
     const int buf = it & 1;
-    const int r0 = tstart + (it % ntr) * BQ;
+    const int r0 = tile_row(it);
     if (it + 1 < nt) load_tile(it + 1);
     const bool active = wave_live && r0 + BQ - 1 >= wr_lo && r0 <= wr_hi;
 
