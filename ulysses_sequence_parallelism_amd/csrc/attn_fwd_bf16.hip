@@ -9,9 +9,9 @@
 // returns O and the natural-log LSE of every row.
 //
 // Design (gfx950):
-//   * Workgroup = 4 waves that share one KV head: HG query heads of the group
-//     times 4/HG blocks of 32 query rows. Each staged K/V tile feeds every
-//     wave, so a K/V byte brought into LDS serves 4*32 query rows.
+//   * Workgroup = 8 waves that share one KV head: HG query heads of the group
+//     times 8/HG blocks of 32 query rows. Each staged K/V tile feeds every
+//     wave, so a K/V byte brought into LDS serves 8*32 query rows.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //     a lane then owns ONE query row (column l%32) and 16 keys per 32-key
 //     block, so the softmax row max / row sum are in-lane reductions plus one
@@ -23,8 +23,12 @@
 //   * Q stays in registers for the whole key loop (8 x 16 bytes per lane).
 //   * K and V^T tiles of 64 keys are double-buffered in LDS (padded pitches:
 //     every 8-lane group of a 16-byte LDS read hits distinct banks); the next
-//     tile's global loads are issued before the current tile's math, one
+//     tiles' global loads are issued before the current tile's math, one
 //     barrier per tile.
+//   * Software pipeline inside each wave: the scores of tile t+1 (MFMA) are
+//     computed in the same straight-line block as the softmax of tile t
+//     (VALU), so the two interleave; boundary tiles and running-max updates
+//     take a rarely used slow path.
 //   * Online softmax in the log2 domain (scale*log2(e) folded into one FMA
 //     before v_exp_f32) with a lazy, exact rescale: the running max is only
 //     raised when a row's tile max exceeds it by more than 8 (log2 units), so
@@ -61,8 +65,8 @@ struct FwdParams {
 };
 
 template <int HG>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams pr) {
-  constexpr int QBW = 4 / HG;
+__global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
+  constexpr int QBW = 8 / HG;
   constexpr int QROWS = 32 * QBW;
   __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][BN * KP];
   __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][D * VP];
@@ -119,67 +123,108 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams pr) {
   const int tstart = (kmin / BN) * BN;
   const int nt = kmax >= kmin ? (kmax - tstart) / BN + 1 : 0;
 
-  // staging: 4 K chunks + 4 V^T chunks of 16 bytes per thread
-  u32x4 stk[4], stv[4];
-  auto load_tile = [&](int t0) {
+  // Software pipeline: the scores of tile t+1 are computed while tile t goes
+  // through the softmax, so one wave's MFMAs and vector work are independent
+  // and can interleave. K runs one tile ahead of V: K(t) is staged into LDS at
+  // the end of iteration t-2 and V(t) at the end of iteration t-1, so each
+  // needs only two LDS slots and there is one barrier per tile.
+  u32x4 stk[2], stv[2];
+  auto load_k = [&](int t) {
+    const int t0 = tstart + t * BN;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = (tid >> 4) + 16 * u, c = tid & 15;
+    for (int u = 0; u < 2; ++u) {
+      const int r = (tid >> 4) + 32 * u, c = tid & 15;
       // keys past the end read the last key (always masked): unconditional loads
       const int j = min(t0 + r, s_pad - 1);
       stk[u] = *reinterpret_cast<const u32x4*>(pr.k + ((int64_t)j * pr.hkv + kvh) * D + c * 8);
-      const int dr = (tid >> 3) + 32 * u, c8 = tid & 7;
+    }
+  };
+  auto load_v = [&](int t) {
+    const int t0 = tstart + t * BN;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int dr = (tid >> 3) + 64 * u, c8 = tid & 7;
       stv[u] = *reinterpret_cast<const u32x4*>(pr.vt + ((int64_t)kvh * D + dr) * pr.s_t + t0 + c8 * 8);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_k = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = (tid >> 4) + 16 * u, c = tid & 15;
+    for (int u = 0; u < 2; ++u) {
+      const int r = (tid >> 4) + 32 * u, c = tid & 15;
       *reinterpret_cast<u32x4*>(&lds_k[buf][r * KP + c * 8]) = stk[u];
-      const int dr = (tid >> 3) + 32 * u, c8 = tid & 7;
+    }
+  };
+  auto store_v = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int dr = (tid >> 3) + 64 * u, c8 = tid & 7;
       *reinterpret_cast<u32x4*>(&lds_v[buf][dr * VP + c8 * 8]) = stv[u];
     }
   };
-
-  if (nt > 0) {
-    load_tile(tstart);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < nt; ++it) {
-    const int t0 = tstart + it * BN;
-    const int buf = it & 1;
-    if (it + 1 < nt) load_tile(t0 + BN);
-
-    if (t0 <= wkmax && t0 + BN - 1 >= wkmin) {
-      // S^T = K Q^T for two 32-key blocks
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  // S^T = K Q^T for the two 32-key blocks of the tile in slot buf
+  auto scores = [&](int buf, f32x16* sacc) {
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const __bf16* kp = &lds_k[buf][(kb * 32 + ln) * KP + hl * 8];
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-          sacc[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kp + kk * 16), qreg[kk], sacc[kb]);
+        sacc[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kp + kk * 16), qreg[kk], sacc[kb]);
       }
-      const bool full = t0 >= free_lo && t0 + BN - 1 <= free_hi;
+    }
+  };
+
+  f32x16 scur[2], snext[2];
+  if (nt > 0) {
+    load_k(0);
+    store_k(0);
+    if (nt > 1) {
+      load_k(1);
+      store_k(1);
+    }
+    load_v(0);
+    store_v(0);
+  }
+  __syncthreads();
+  if (nt > 0) scores(0, scur);
+  __syncthreads();  // S(0) is read from slot 0 before iteration 0 refills it
+
+  for (int it = 0; it < nt; ++it) {
+    const int t0 = tstart + it * BN;
+    if (it + 2 < nt) load_k(it + 2);
+    if (it + 1 < nt) load_v(it + 1);
+
+    // -- row max of this tile; a full tile needs no mask
+    float m4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x16& a = scur[q >> 1];
+      const int o = (q & 1) * 8;
+      m4[q] = fmaxf(fmaxf(fmaxf(a[o], a[o + 1]), fmaxf(a[o + 2], a[o + 3])),
+                    fmaxf(fmaxf(a[o + 4], a[o + 5]), fmaxf(a[o + 6], a[o + 7])));
+    }
+    float mx = half_swap_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * pr.scale_log2;
+    const bool full = t0 >= free_lo && t0 + BN - 1 <= free_hi &&
+                      t0 >= wkmin && t0 + BN - 1 <= wkmax;
+    // -- slow path (boundary tiles and running-max updates, both rare): mask,
+    //    recompute the max, rescale O
+    if (__ballot(!full || mx > m_run + kRescaleThreshold)) {
       if (!full) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = t0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-            if (key < lo || key > hi) sacc[kb][i] = -INFINITY;
+            if (key < lo || key > hi) scur[kb][i] = -INFINITY;
           }
+        float m = scur[0][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) m = fmaxf(m, scur[0][i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, scur[1][i]);
+        mx = half_swap_max(m) * pr.scale_log2;
       }
-      // row max of this tile (raw scores), across both half-waves
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[0][i]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[1][i]);
-      mx = half_swap_max(mx) * pr.scale_log2;
       const bool need = mx > m_run + kRescaleThreshold;
       if (__ballot(need)) {
         const float mnew = need ? mx : m_run;
@@ -191,37 +236,49 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams pr) {
         l_run *= alpha;
         m_run = mnew;
       }
-      const float msub = m_run == -INFINITY ? 0.f : m_run;
-      bf16x8 pb[4];
-      float lsum = 0.f;
+    }
+    const float msub = m_run == -INFINITY ? 0.f : m_run;
+
+    // -- one straight-line block: the next tile's scores (MFMA; its slot holds
+    //    stale data on the last iteration and the result is then unused) and
+    //    this tile's probabilities (VALU) are independent and interleave
+    scores((it + 1) & 1, snext);
+    bf16x8 pb[4];
+    float ls4[4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          u32x4 pk;
+      for (int c = 0; c < 2; ++c) {
+        u32x4 pk;
+        float ls = 0.f;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * c + 2 * t], pr.scale_log2, -msub));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * c + 2 * t + 1], pr.scale_log2, -msub));
-            lsum += p0 + p1;
-            pk[t] = pack_bf16x2(p0, p1);
-          }
-          pb[kb * 2 + c] = __builtin_bit_cast(bf16x8, pk);
+        for (int t = 0; t < 4; ++t) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][8 * c + 2 * t], pr.scale_log2, -msub));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][8 * c + 2 * t + 1], pr.scale_log2, -msub));
+          ls += p0 + p1;
+          pk[t] = pack_bf16x2(p0, p1);
         }
+        ls4[kb * 2 + c] = ls;
+        pb[kb * 2 + c] = __builtin_bit_cast(bf16x8, pk);
       }
-      l_run += lsum;
-      // O^T += V^T P^T
+    }
+    l_run += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
+
+    // -- O^T += V^T P^T
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const __bf16* vp = &lds_v[buf][(b * 32 + ln) * VP + hl * 8];
-#pragma unroll
-        for (int ch = 0; ch < 4; ++ch)
-          oacc[b] = mfma32(*reinterpret_cast<const bf16x8*>(vp + ch * 16), pb[ch], oacc[b]);
+        const __bf16* vp = &lds_v[it & 1][(b * 32 + ln) * VP + hl * 8];
+        oacc[b] = mfma32(*reinterpret_cast<const bf16x8*>(vp + ch * 16), pb[ch], oacc[b]);
       }
     }
 
-    if (it + 1 < nt) store_tile(buf ^ 1);
+    if (it + 2 < nt) store_k(it & 1);
+    if (it + 1 < nt) store_v((it + 1) & 1);
     __syncthreads();
+    scur[0] = snext[0];
+    scur[1] = snext[1];
   }
 
   const float l_tot = half_swap_sum(l_run);
@@ -243,12 +300,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams pr) {
 
 template <int HG>
 int launch_fwd(const FwdParams& p, int g, int hkv, hipStream_t stream) {
-  constexpr int QROWS = 32 * (4 / HG);
+  constexpr int QROWS = 32 * (8 / HG);
   FwdParams pr = p;
   pr.n_qblocks = (p.s_pad + QROWS - 1) / QROWS;
   dim3 grid((unsigned)pr.n_qblocks, (unsigned)(hkv * (g / HG)));
   TraceScope ts("attn_fwd_bf16", stream);
-  hipLaunchKernelGGL((fwd_bf16_kernel<HG>), grid, dim3(256), 0, stream, pr);
+  hipLaunchKernelGGL((fwd_bf16_kernel<HG>), grid, dim3(512), 0, stream, pr);
   return hipGetLastError() == hipSuccess ? USP_OK : USP_ERR_HIP;
 }
 
