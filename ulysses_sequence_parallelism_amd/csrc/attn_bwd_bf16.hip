@@ -25,6 +25,8 @@
 //   * Tiles are double-buffered in LDS with padded pitches, masks are applied
 //     only on boundary tiles, and the causal triangle is launched
 //     heaviest-first.
+#include <type_traits>
+
 #include "usp_common.h"
 #include "usp_internal.h"
 
@@ -240,25 +242,33 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
           pa[mb] = mfma32(*reinterpret_cast<const bf16x8*>(ap + kk * 16), sreg[kk], pa[mb]);
       }
       if (role == 0) {
-        // rows [mlo, mhi) keep their probability; a mask-free tile uses a
-        // range that contains every row of the tile
+        // P = exp2(S*scale*log2e - LSE*log2e); masked entries are 0. Most
+        // tiles need no mask, so the mask test is kept off their path.
         const bool full = all_keys_valid && r0 >= free_lo && r0 + BQ - 1 <= free_hi;
-        const int mlo = full ? r0 : (key_ok ? rlo : s_pad);
-        const int mhi = full ? r0 + BQ : (key_ok ? rhi : 0);
+        auto probs = [&](auto masked) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
+          for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int rr = mb * 32 + r4 * 8 + hl * 4;  // first of 4 consecutive rows
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&llse[buf][rr]);
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const int rr = mb * 32 + r4 * 8 + hl * 4;  // first of 4 consecutive rows
+              const f32x4 l4 = *reinterpret_cast<const f32x4*>(&llse[buf][rr]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = r4 * 4 + e;
-              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(pa[mb][i], pr.scale_log2, -l4[e]));
-              const int row = r0 + rr + e;
-              pa[mb][i] = (row >= mlo && row < mhi) ? p : 0.f;
+              for (int e = 0; e < 4; ++e) {
+                const int i = r4 * 4 + e;
+                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(pa[mb][i], pr.scale_log2, -l4[e]));
+                if constexpr (decltype(masked)::value) {
+                  const int row = r0 + rr + e;
+                  p = (key_ok && row >= rlo && row < rhi) ? p : 0.f;
+                }
+                pa[mb][i] = p;
+              }
             }
           }
+        };
+        if (full) probs(std::false_type{});
+        else probs(std::true_type{});
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             u32x4 a;
@@ -279,16 +289,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
         for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            const u32x4 praw = lp[grp][mb * 2 + c][lane];
-            const bf16x8 pv = __builtin_bit_cast(bf16x8, praw);
+            const bf16x8 pv = __builtin_bit_cast(bf16x8, lp[grp][mb * 2 + c][lane]);
             const f32x4 d4a = *reinterpret_cast<const f32x4*>(&ldd[buf][mb * 32 + (2 * c) * 8 + hl * 4]);
             const f32x4 d4b = *reinterpret_cast<const f32x4*>(&ldd[buf][mb * 32 + (2 * c + 1) * 8 + hl * 4]);
             u32x4 o;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const int i0 = 8 * c + 2 * t, i1 = i0 + 1;  // accumulator registers
-              const float dd0 = (i0 >> 2) == 2 * c ? d4a[i0 & 3] : d4b[i0 & 3];
-              const float dd1 = (i1 >> 2) == 2 * c ? d4a[i1 & 3] : d4b[i1 & 3];
+              // registers 8c..8c+3 pair with D rows of d4a, 8c+4..8c+7 with d4b
+              const float dd0 = t < 2 ? d4a[2 * t] : d4b[2 * t - 4];
+              const float dd1 = t < 2 ? d4a[2 * t + 1] : d4b[2 * t - 3];
               const float p0 = (float)pv[2 * t], p1 = (float)pv[2 * t + 1];
               o[t] = pack_bf16x2(p0 * (pa[mb][i0] - dd0), p1 * (pa[mb][i1] - dd1));
             }
@@ -440,18 +450,27 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
         }
       }
       const bool full = t0 >= free_lo && t0 + BN - 1 <= free_hi;
-      const int mlo = full ? t0 : lo;
-      const int mhi = full ? t0 + BN - 1 : hi;
+      // dS^T = P^T (dP^T - D); most tiles need no mask, so the mask test is
+      // kept off their path
+      auto dsoft = [&](auto masked) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[kb][i], pr.scale_log2, -lse2));
+            if constexpr (decltype(masked)::value) {
+              const int key = t0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+              p = (key >= lo && key <= hi) ? p : 0.f;
+            }
+            pa[kb][i] = p * (pa[kb][i] - drow);
+          }
+        }
+      };
+      if (full) dsoft(std::false_type{});
+      else dsoft(std::true_type{});
       bf16x8 dst[2 * KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[kb][i], pr.scale_log2, -lse2));
-          const int key = t0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-          p = (key >= mlo && key <= mhi) ? p : 0.f;
-          pa[kb][i] = p * (pa[kb][i] - drow);
-        }
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           u32x4 b;
