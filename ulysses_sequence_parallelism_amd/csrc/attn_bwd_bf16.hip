@@ -225,7 +225,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
   for (int it = 0; it < nt; ++it) {
     const int buf = it & 1;
     const int r0 = tile_row(it);
-    if (it + 1 < nt) load_tile(it + 1);
     const bool active = wave_live && r0 + BQ - 1 >= wr_lo && r0 <= wr_hi;
 
     // phase 1: role 0 -> P (to LDS and registers); role 1 -> dP (registers)
@@ -235,11 +234,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
       const __bf16* base = role == 0 ? lq[buf] : ldo[buf];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        pa[mb] = f32x16{};
+        // all 8 A fragments of the block are requested before its MFMA chain,
+        // so the chain waits for one LDS round trip, not one per MFMA pair
         const __bf16* ap = base + (mb * 32 + ln) * KP + hl * 8;
+        bf16x8 af[8];
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-          pa[mb] = mfma32(*reinterpret_cast<const bf16x8*>(ap + kk * 16), sreg[kk], pa[mb]);
+        for (int kk = 0; kk < 8; ++kk) af[kk] = *reinterpret_cast<const bf16x8*>(ap + kk * 16);
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the chain
+        pa[mb] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) pa[mb] = mfma32(af[kk], sreg[kk], pa[mb]);
       }
       if (role == 0) {
         // P = exp2(S*scale*log2e - LSE*log2e); masked entries are 0. Most
@@ -281,6 +285,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
       }
     }
     __syncthreads();  // P is visible to role 1
+    // next tile's global loads: issued here so their registers are not live
+    // during phase 1; phase 2 covers their latency
+    if (it + 1 < nt) load_tile(it + 1);
 
     // phase 2: role 0 -> dV^T += dO^T P; role 1 -> dS, dK^T += Q^T dS
     if (active) {
@@ -308,11 +315,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
       }
       const __bf16* tbase = role == 0 ? ldot[buf] : lqt[buf];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const __bf16* tp = tbase + (b * 32 + ln) * TQ + hl * 8;
+      for (int b2 = 0; b2 < 4; b2 += 2) {
+        // fragments of two output blocks requested together (see above)
+        bf16x8 af[2][NCH];
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const __bf16* tp = tbase + ((b2 + bb) * 32 + ln) * TQ + hl * 8;
+#pragma unroll
+          for (int ch = 0; ch < NCH; ++ch) af[bb][ch] = *reinterpret_cast<const bf16x8*>(tp + ch * 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the chain
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch)
-          acc[b] = mfma32(*reinterpret_cast<const bf16x8*>(tp + ch * 16), pb[ch], acc[b]);
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb) acc[b2 + bb] = mfma32(af[bb][ch], pb[ch], acc[b2 + bb]);
       }
     }
     if (it + 1 < nt) store_tile(buf ^ 1);
@@ -439,15 +455,22 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
       f32x16 sa[KB], pa[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        sa[kb] = f32x16{};
-        pa[kb] = f32x16{};
+        // the A fragments of each chain are requested before the chain runs
         const __bf16* kp = &lk[buf][(kb * 32 + ln) * KP + hl * 8];
         const __bf16* vp = &lv[buf][(kb * 32 + ln) * KP + hl * 8];
+        bf16x8 af[8];
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          sa[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kp + kk * 16), qreg[kk], sa[kb]);
-          pa[kb] = mfma32(*reinterpret_cast<const bf16x8*>(vp + kk * 16), doreg[kk], pa[kb]);
-        }
+        for (int kk = 0; kk < 8; ++kk) af[kk] = *reinterpret_cast<const bf16x8*>(kp + kk * 16);
+        __builtin_amdgcn_sched_barrier(0);
+        sa[kb] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) sa[kb] = mfma32(af[kk], qreg[kk], sa[kb]);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) af[kk] = *reinterpret_cast<const bf16x8*>(vp + kk * 16);
+        __builtin_amdgcn_sched_barrier(0);
+        pa[kb] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) pa[kb] = mfma32(af[kk], doreg[kk], pa[kb]);
       }
       const bool full = t0 >= free_lo && t0 + BN - 1 <= free_hi;
       // dS^T = P^T (dP^T - D); most tiles need no mask, so the mask test is
@@ -480,12 +503,19 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
         }
       }
       // dQ^T += K^T dS^T (rows = d, cols = queries)
+      {
+        bf16x8 af[4][2 * KB];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const __bf16* tp = &lkt[buf][(b * 32 + ln) * TK + hl * 8];
+        for (int b = 0; b < 4; ++b) {
+          const __bf16* tp = &lkt[buf][(b * 32 + ln) * TK + hl * 8];
+#pragma unroll
+          for (int ch = 0; ch < 2 * KB; ++ch) af[b][ch] = *reinterpret_cast<const bf16x8*>(tp + ch * 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ch = 0; ch < 2 * KB; ++ch)
-          dqa[b] = mfma32(*reinterpret_cast<const bf16x8*>(tp + ch * 16), dst[ch], dqa[b]);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) dqa[b] = mfma32(af[b][ch], dst[ch], dqa[b]);
       }
     }
     if (it + 1 < nt) store_tile(buf ^ 1);

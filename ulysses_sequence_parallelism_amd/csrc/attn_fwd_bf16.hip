@@ -175,7 +175,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
     }
   };
 
-  f32x16 scur[2], snext[2];
+  f32x16 sa[2], sb[2];
   if (nt > 0) {
     load_k(0);
     store_k(0);
@@ -187,98 +187,102 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
     store_v(0);
   }
   __syncthreads();
-  if (nt > 0) scores(0, scur);
+  if (nt > 0) scores(0, sa);
   __syncthreads();  // S(0) is read from slot 0 before iteration 0 refills it
 
-  for (int it = 0; it < nt; ++it) {
-    const int t0 = tstart + it * BN;
-    if (it + 2 < nt) load_k(it + 2);
-    if (it + 1 < nt) load_v(it + 1);
+  // one pipeline step; the score buffers swap roles every step, so the loop
+  // is unrolled by two instead of copying the next scores over the current
+  auto step = [&](int it, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+      const int t0 = tstart + it * BN;
+      if (it + 2 < nt) load_k(it + 2);
+      if (it + 1 < nt) load_v(it + 1);
 
-    // -- row max of this tile; a full tile needs no mask
-    float m4[4];
+      // -- row max of this tile; a full tile needs no mask
+      float m4[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x16& a = scur[q >> 1];
-      const int o = (q & 1) * 8;
-      m4[q] = fmaxf(fmaxf(fmaxf(a[o], a[o + 1]), fmaxf(a[o + 2], a[o + 3])),
-                    fmaxf(fmaxf(a[o + 4], a[o + 5]), fmaxf(a[o + 6], a[o + 7])));
-    }
-    float mx = half_swap_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * pr.scale_log2;
-    const bool full = t0 >= free_lo && t0 + BN - 1 <= free_hi &&
-                      t0 >= wkmin && t0 + BN - 1 <= wkmax;
-    // -- slow path (boundary tiles and running-max updates, both rare): mask,
-    //    recompute the max, rescale O
-    if (__ballot(!full || mx > m_run + kRescaleThreshold)) {
-      if (!full) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = t0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-            if (key < lo || key > hi) scur[kb][i] = -INFINITY;
-          }
-        float m = scur[0][0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) m = fmaxf(m, scur[0][i]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) m = fmaxf(m, scur[1][i]);
-        mx = half_swap_max(m) * pr.scale_log2;
+      for (int q = 0; q < 4; ++q) {
+        const f32x16& a = scur[q >> 1];
+        const int o = (q & 1) * 8;
+        m4[q] = fmaxf(fmaxf(fmaxf(a[o], a[o + 1]), fmaxf(a[o + 2], a[o + 3])),
+                      fmaxf(fmaxf(a[o + 4], a[o + 5]), fmaxf(a[o + 6], a[o + 7])));
       }
-      const bool need = mx > m_run + kRescaleThreshold;
-      if (__ballot(need)) {
-        const float mnew = need ? mx : m_run;
-        const float alpha = need ? exp2f(m_run - mnew) : 1.f;
+      float mx = half_swap_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * pr.scale_log2;
+      const bool full = t0 >= free_lo && t0 + BN - 1 <= free_hi &&
+                        t0 >= wkmin && t0 + BN - 1 <= wkmax;
+      // -- slow path (boundary tiles and running-max updates, both rare): mask,
+      //    recompute the max, rescale O
+      if (__ballot(!full || mx > m_run + kRescaleThreshold)) {
+        if (!full) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
-        l_run *= alpha;
-        m_run = mnew;
-      }
-    }
-    const float msub = m_run == -INFINITY ? 0.f : m_run;
-
-    // -- one straight-line block: the next tile's scores (MFMA; its slot holds
-    //    stale data on the last iteration and the result is then unused) and
-    //    this tile's probabilities (VALU) are independent and interleave
-    scores((it + 1) & 1, snext);
-    bf16x8 pb[4];
-    float ls4[4];
+            for (int i = 0; i < 16; ++i) {
+              const int key = t0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+              if (key < lo || key > hi) scur[kb][i] = -INFINITY;
+            }
+          float m = scur[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+          for (int i = 1; i < 16; ++i) m = fmaxf(m, scur[0][i]);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        u32x4 pk;
-        float ls = 0.f;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][8 * c + 2 * t], pr.scale_log2, -msub));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][8 * c + 2 * t + 1], pr.scale_log2, -msub));
-          ls += p0 + p1;
-          pk[t] = pack_bf16x2(p0, p1);
+          for (int i = 0; i < 16; ++i) m = fmaxf(m, scur[1][i]);
+          mx = half_swap_max(m) * pr.scale_log2;
         }
-        ls4[kb * 2 + c] = ls;
-        pb[kb * 2 + c] = __builtin_bit_cast(bf16x8, pk);
-      }
-    }
-    l_run += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
-
-    // -- O^T += V^T P^T
+        const bool need = mx > m_run + kRescaleThreshold;
+        if (__ballot(need)) {
+          const float mnew = need ? mx : m_run;
+          const float alpha = need ? exp2f(m_run - mnew) : 1.f;
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
+          for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const __bf16* vp = &lds_v[it & 1][(b * 32 + ln) * VP + hl * 8];
-        oacc[b] = mfma32(*reinterpret_cast<const bf16x8*>(vp + ch * 16), pb[ch], oacc[b]);
+            for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
+          l_run *= alpha;
+          m_run = mnew;
+        }
       }
-    }
+      const float msub = m_run == -INFINITY ? 0.f : m_run;
 
-    if (it + 2 < nt) store_k(it & 1);
-    if (it + 1 < nt) store_v((it + 1) & 1);
-    __syncthreads();
-    scur[0] = snext[0];
-    scur[1] = snext[1];
+      // -- one straight-line block: the next tile's scores (MFMA; its slot holds
+      //    stale data on the last iteration and the result is then unused) and
+      //    this tile's probabilities (VALU) are independent and interleave
+      scores((it + 1) & 1, snext);
+      bf16x8 pb[4];
+      float ls4[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          u32x4 pk;
+          float ls = 0.f;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][8 * c + 2 * t], pr.scale_log2, -msub));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][8 * c + 2 * t + 1], pr.scale_log2, -msub));
+            ls += p0 + p1;
+            pk[t] = pack_bf16x2(p0, p1);
+          }
+          ls4[kb * 2 + c] = ls;
+          pb[kb * 2 + c] = __builtin_bit_cast(bf16x8, pk);
+        }
+      }
+      l_run += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
+
+      // -- O^T += V^T P^T
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const __bf16* vp = &lds_v[it & 1][(b * 32 + ln) * VP + hl * 8];
+          oacc[b] = mfma32(*reinterpret_cast<const bf16x8*>(vp + ch * 16), pb[ch], oacc[b]);
+        }
+      }
+
+      if (it + 2 < nt) store_k(it & 1);
+      if (it + 1 < nt) store_v((it + 1) & 1);
+      __syncthreads();
+  };
+  for (int it = 0; it < nt; it += 2) {
+    step(it, sa, sb);
+    if (it + 1 < nt) step(it + 1, sb, sa);
   }
 
   const float l_tot = half_swap_sum(l_run);
