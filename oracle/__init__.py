@@ -11,7 +11,10 @@ Contents
              written out from their index definitions.
   attention  exact grouped-query attention forward (textbook softmax over
              materialised score rows) and its closed-form backward, with the
-             causal, key-padding and packed-document masks.
+             causal, key-padding and packed-document masks; attention between
+             a query interval and a key interval (global positions), the
+             log-sum-exp merge of partial results, and the per-interval
+             backward contributions.
 
 Pins (see tests/test_oracle_*.py): a hand-derived worked example
 (tests/golden), torch's float64 scaled_dot_product_attention with autograd
@@ -29,6 +32,9 @@ from .attention import (
     attn_fwd_rows,
     attn_bwd_rows,
     attn_bwd_keys,
+    attn_fwd_partial,
+    attn_bwd_partial,
+    lse_merge,
 )
 
 __all__ = [
@@ -42,4 +48,7 @@ __all__ = [
     "attn_fwd_rows",
     "attn_bwd_rows",
     "attn_bwd_keys",
+    "attn_fwd_partial",
+    "attn_bwd_partial",
+    "lse_merge",
 ]

@@ -218,3 +218,115 @@ def attn_bwd_keys(q, k, v, do, keys, scale, s_valid=None, cu_seqlens=None, causa
             dk[sel, kvh, :] += scale * (ds[:, ks].T @ q[rb, h, :])
             dv[sel, kvh, :] += p[:, ks].T @ do[rb, h, :]
     return dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Attention between a query interval and a key interval of one sequence, and
+# the merge of partial results. Ring / USP sequence parallelism splits the key
+# axis into chunks that visit every rank's queries ("feat(dspark): add Ulysses
+# sequence parallel training", Modifications, names ring sequence parallelism
+# as the next step; "[trainer] feat: support sequence parallel", review
+# overview, builds a (dp, ring, ulysses) mesh); contiguous context parallelism
+# gives each rank a contiguous interval of query rows against the whole key
+# sequence with causal offsets ("GLM-5.2 131k context parallelism", Purpose:
+# contiguous partition mode, q_causal_offsets).
+#
+# Query row i of the buffer sits at global position q_off + i, key row j at
+# k_off + j. Key j is allowed for row i iff j < sk_valid, both positions lie in
+# the same document (cu_seqlens over GLOBAL positions) and, when causal,
+# k_off + j <= q_off + i. A row with no allowed key has LSE = -inf and O = 0.
+
+def _partial_mask(rows, sk, q_off, k_off, sk_valid, doc, causal):
+    gi = q_off + rows
+    gj = k_off + np.arange(sk)
+    m = np.broadcast_to(np.arange(sk)[None, :] < sk_valid, (len(rows), sk)).copy()
+    if causal:
+        m &= gj[None, :] <= gi[:, None]
+    if doc is not None:
+        m &= doc[gj][None, :] == doc[gi][:, None]
+    return m
+
+
+def attn_fwd_partial(q, k, v, scale, q_off=0, k_off=0, sk_valid=None, cu_seqlens=None,
+                     causal=True):
+    """Partial attention of a query interval against a key interval:
+    (O [sq, Hq, d], LSE [Hq, sq]); rows without any allowed key get O = 0 and
+    LSE = -inf."""
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    sq, hq, d = q.shape
+    sk, hkv = k.shape[0], k.shape[1]
+    g = hq // hkv
+    sk_valid = sk if sk_valid is None else sk_valid
+    doc = None
+    if cu_seqlens is not None:
+        doc = doc_of(int(np.asarray(cu_seqlens)[-1]), cu_seqlens)
+    o = np.zeros((sq, hq, d))
+    lse = np.full((hq, sq), -np.inf)
+    for b0 in range(0, sq, ROW_BLOCK):
+        rb = np.arange(b0, min(sq, b0 + ROW_BLOCK))
+        allowed = _partial_mask(rb, sk, q_off, k_off, sk_valid, doc, causal)
+        live = allowed.any(axis=1)
+        for h in range(hq):
+            z = scale * (q[rb, h, :] @ k[:, h // g, :].T)
+            z[~allowed] = -np.inf
+            zl = z[live]
+            if zl.size == 0:
+                continue
+            m = zl.max(axis=1)
+            lse_b = m + np.log(np.exp(zl - m[:, None]).sum(axis=1))
+            p = np.exp(zl - lse_b[:, None])
+            o[rb[live], h, :] = p @ v[:, h // g, :]
+            lse[h, rb[live]] = lse_b
+    return o, lse
+
+
+def lse_merge(parts):
+    """Merge partial results [(O_r, LSE_r), ...] over disjoint key sets:
+    LSE = log sum_r exp(LSE_r), O = sum_r exp(LSE_r - LSE) O_r (rows where
+    every LSE_r is -inf stay O = 0, LSE = -inf)."""
+    lses = np.stack([np.asarray(l, dtype=np.float64) for _, l in parts])   # [R, Hq, sq]
+    m = lses.max(axis=0)
+    msafe = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(lses - msafe[None])                                          # [R, Hq, sq]
+    tot = w.sum(axis=0)
+    lse = np.where(tot > 0, msafe + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)
+    o = np.zeros_like(np.asarray(parts[0][0], dtype=np.float64))
+    for (o_r, _), w_r in zip(parts, w):
+        o += np.where(tot > 0, w_r / np.where(tot > 0, tot, 1.0), 0.0).T[:, :, None] * o_r
+    return o, lse
+
+
+def attn_bwd_partial(q, k, v, o, lse, do, scale, q_off=0, k_off=0, sk_valid=None,
+                     cu_seqlens=None, causal=True):
+    """Backward contributions of one key interval given the FINAL output O and
+    the FINAL (merged) LSE of the query rows: (dQ [sq, Hq, d] from these keys
+    only, dK and dV [sk, Hkv, d] from these query rows only). Summing dQ over
+    the key intervals and dK, dV over the query intervals gives the full
+    gradients; D_i = dO_i . O_i uses the final O."""
+    q, k, v, o, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, o, do))
+    lse = np.asarray(lse, dtype=np.float64)
+    sq, hq, d = q.shape
+    sk, hkv = k.shape[0], k.shape[1]
+    g = hq // hkv
+    sk_valid = sk if sk_valid is None else sk_valid
+    doc = None
+    if cu_seqlens is not None:
+        doc = doc_of(int(np.asarray(cu_seqlens)[-1]), cu_seqlens)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b0 in range(0, sq, ROW_BLOCK):
+        rb = np.arange(b0, min(sq, b0 + ROW_BLOCK))
+        allowed = _partial_mask(rb, sk, q_off, k_off, sk_valid, doc, causal)
+        for h in range(hq):
+            kvh = h // g
+            z = scale * (q[rb, h, :] @ k[:, kvh, :].T)
+            lrow = lse[h, rb]
+            p = np.where(allowed, np.exp(np.where(allowed, z, 0.0) - np.where(np.isfinite(lrow), lrow, 0.0)[:, None]), 0.0)
+            dp = do[rb, h, :] @ v[:, kvh, :].T
+            dd = (do[rb, h, :] * o[rb, h, :]).sum(axis=1)
+            ds = p * (dp - dd[:, None])
+            dq[rb, h, :] = scale * (ds @ k[:, kvh, :])
+            dk[:, kvh, :] += scale * (ds.T @ q[rb, h, :])
+            dv[:, kvh, :] += p.T @ do[rb, h, :]
+    return dq, dk, dv
