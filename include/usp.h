@@ -148,6 +148,91 @@ int usp_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                  void* stream);
 
 /*
+ * Attention between a query interval and a key interval on global positions:
+ * the partial result of one ring step of Ring / USP attention (the ring degree
+ * of USP: "feat(dspark)", Accuracy Test; "[trainer] feat: support sequence
+ * parallel", review overview, the (dp, ring, ulysses) device mesh), or a
+ * contiguous context-parallel rank's query rows against the whole key sequence
+ * with a causal offset ("GLM-5.2 131k context parallelism", Purpose: causal
+ * query offsets and positions from global cu_seqlens over each rank's
+ * contiguous row interval).
+ * Query row i sits at global position q_off + i (i < s_q), key j at k_off + j
+ * (j < s_k). The allowed keys of row i are
+ *     M(i) = { j < s_k_valid, doc(k_off + j) == doc(q_off + i), and
+ *              k_off + j <= q_off + i when causal }
+ * with doc() from cu_seqlens over GLOBAL positions (one document when NULL).
+ * Then, as in usp_attn_fwd, lse[h][i] = log sum_{j in M(i)} exp(scale q_i.k_j)
+ * and o[i][h] = sum_{j in M(i)} exp(scale q_i.k_j - lse[h][i]) v_j; a row with
+ * M(i) empty gets o = 0 and lse = -inf (the identity of usp_attn_merge).
+ * usp_attn_fwd(...) equals this call with s_q = s_k = s_pad, q_off = k_off = 0.
+ *   q: [s_q][hq][d], k and v: [s_k][hkv][d] (dtype), read only.
+ *   o: [s_q][hq][d] in o_dtype (USP_FP32 for a partial that will be merged,
+ *     USP_BF16 allowed for bf16 inputs); lse: [hq][s_q] fp32. Both overwritten.
+ *   cu_seqlens: device int32 [n_docs + 1], 0 = cu[0] <= ... <= cu[n_docs], and
+ *     cu[n_docs] >= q_off + s_q and >= k_off + s_k; or NULL. Not checked.
+ *   workspace: usp_attn_fwd_workspace_bytes(s_k, hq, hkv, d, dtype) bytes.
+ * Errors: USP_ERR_INVALID for s_q < 1, s_k < 1, negative offsets,
+ * q_off + s_q or k_off + s_k >= 2^30, s_k_valid outside [0, s_k], the head and
+ * scale checks of usp_attn_fwd, misalignment or aliasing; USP_ERR_UNSUPPORTED
+ * for d / dtype as in usp_attn_fwd, or o_dtype USP_BF16 with fp32 inputs.
+ */
+int usp_attn_fwd_interval(const void* q, const void* k, const void* v, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes,
+                          int64_t s_q, int64_t q_off, int64_t s_k, int64_t k_off,
+                          int64_t s_k_valid, const int32_t* cu_seqlens, int n_docs,
+                          int hq, int hkv, int d, float softmax_scale, int causal, int dtype,
+                          int o_dtype, void* stream);
+
+/*
+ * Exact merge of two partial results over disjoint key sets of the same query
+ * rows (combining the ring steps of Ring / USP attention; same sources as
+ * usp_attn_fwd_interval):
+ *     lse = log(exp(lse_a) + exp(lse_b))
+ *     o   = exp(lse_a - lse) o_a + exp(lse_b - lse) o_b
+ * Rows with lse_a = lse_b = -inf give o = 0, lse = -inf.
+ *   o_a, o_b: [s_q][hq][d] fp32; lse_a, lse_b: [hq][s_q] fp32; read only.
+ *   o: [s_q][hq][d] in o_dtype; lse: [hq][s_q] fp32; overwritten. For in-place
+ *     accumulation o may BE o_a or o_b (same pointer, o_dtype USP_FP32) and lse
+ *     may BE lse_a or lse_b; any other overlap is rejected.
+ * Supported: d in {64, 128}. Errors: USP_ERR_INVALID for s_q < 1, hq < 1,
+ * s_q * hq * d >= 2^31, misalignment or partial overlap; USP_ERR_UNSUPPORTED
+ * for other d or o_dtype; USP_ERR_NULL for NULL pointers.
+ */
+int usp_attn_merge(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
+                   void* o, float* lse, int64_t s_q, int hq, int d, int o_dtype, void* stream);
+
+/* Workspace bytes usp_attn_bwd_interval needs for these sizes. */
+size_t usp_attn_bwd_interval_workspace_bytes(int64_t s_q, int64_t s_k, int hq, int hkv, int d,
+                                             int dtype);
+
+/*
+ * Backward of one (query interval, key interval) pair, given the FINAL output o
+ * and the FINAL (merged) lse of the query rows: the pair's contributions
+ *     dq_i = scale sum_{j in M(i)} dS_ij k_j
+ *     dk_j = scale sum_{heads of the group} sum_i dS_ij q_i
+ *     dv_j = sum_{heads of the group} sum_i P_ij dout_i
+ * with M(i), P, dP, D = dout_i . o_i and dS = P (dP - D) as in usp_attn_bwd and
+ * usp_attn_fwd_interval. Summing dq over the key intervals of a row and dk, dv
+ * over the query intervals of a key gives the full gradients (the gradient
+ * parity of "feat(dspark)", Accuracy Test, carried over to the ring steps).
+ * usp_attn_bwd(...) equals this call with full intervals and accumulate = 0.
+ *   q, o, dout: [s_q][hq][d]; k, v: [s_k][hkv][d] (dtype); lse: [hq][s_q] fp32.
+ *   dq: [s_q][hq][d]; dk, dv: [s_k][hkv][d]; in grad_dtype. With accumulate = 1
+ *     (grad_dtype USP_FP32 only) the contributions are ADDED to the existing
+ *     contents, else they overwrite them.
+ *   workspace: usp_attn_bwd_interval_workspace_bytes() bytes of scratch.
+ * Errors as usp_attn_fwd_interval; USP_ERR_INVALID also for accumulate not in
+ * {0, 1} or accumulate with bf16 gradients.
+ */
+int usp_attn_bwd_interval(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes,
+                          int64_t s_q, int64_t q_off, int64_t s_k, int64_t k_off,
+                          int64_t s_k_valid, const int32_t* cu_seqlens, int n_docs,
+                          int hq, int hkv, int d, float softmax_scale, int causal, int dtype,
+                          int grad_dtype, int accumulate, void* stream);
+
+/*
  * Kernel tracing (profiling aid, off by default). While enabled, every kernel
  * the library launches is bracketed by a pair of HIP events recorded on its
  * stream. usp_trace_collect() waits for the recorded events, returns per-kernel

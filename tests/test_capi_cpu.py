@@ -51,7 +51,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.usp_version() == 100
+    assert L.usp_version() == 110
     for s in (OK, INVALID, UNSUPPORTED, NULLP, HIPERR, WORKSPACE, 12345):
         assert isinstance(L.usp_status_string(s), bytes)
     assert L.usp_status_string(0) == b"ok"
@@ -148,6 +148,80 @@ def test_attention_null_and_alias(L):
     assert bwd(L, ptrs=p) == NULLP
 
 
+def fwd_iv(L, s_q=200, q_off=0, s_k=256, k_off=0, s_kv=256, cu=None, n_docs=0, hq=4, hkv=1,
+           d=128, scale=0.088, causal=1, dt=BF16, odt=FP32, ws=3 << 30, ws_bytes=1 << 30,
+           ptrs=None):
+    q, k, v, o, lse = ptrs or (A, A + (1 << 24), A + (2 << 24), A + (3 << 24), A + (4 << 24))
+    return L.usp_attn_fwd_interval(*(ctypes.c_void_p(x) for x in (q, k, v, o, lse, ws)), ws_bytes,
+                                   s_q, q_off, s_k, k_off, s_kv, ctypes.c_void_p(cu), n_docs, hq,
+                                   hkv, d, scale, causal, dt, odt, None)
+
+
+def bwd_iv(L, s_q=200, q_off=0, s_k=256, k_off=0, s_kv=256, cu=None, n_docs=0, hq=4, hkv=1,
+           d=128, scale=0.088, causal=1, dt=BF16, gdt=FP32, acc=1, ws=3 << 30,
+           ws_bytes=1 << 30, ptrs=None):
+    ptrs = ptrs or [A + (i << 24) for i in range(9)]
+    return L.usp_attn_bwd_interval(*(ctypes.c_void_p(x) for x in ptrs), ctypes.c_void_p(ws),
+                                   ws_bytes, s_q, q_off, s_k, k_off, s_kv, ctypes.c_void_p(cu),
+                                   n_docs, hq, hkv, d, scale, causal, dt, gdt, acc, None)
+
+
+@pytest.mark.parametrize("f", [fwd_iv, bwd_iv])
+def test_interval_argument_errors(L, f):
+    assert f(L, s_q=0) == INVALID
+    assert f(L, s_k=0, s_kv=0) == INVALID
+    assert f(L, q_off=-1) == INVALID
+    assert f(L, k_off=-5) == INVALID
+    assert f(L, q_off=(1 << 30) - 100) == INVALID       # global positions are 32-bit
+    assert f(L, k_off=(1 << 30) - 100) == INVALID
+    assert f(L, s_kv=-1) == INVALID
+    assert f(L, s_kv=257) == INVALID
+    assert f(L, hq=6, hkv=4) == INVALID
+    assert f(L, cu=A + (8 << 24), n_docs=0) == INVALID
+    assert f(L, cu=A + (8 << 24) + 2, n_docs=2) == INVALID
+    assert f(L, d=64) == UNSUPPORTED
+    assert f(L, dt=3) == UNSUPPORTED
+    assert f(L, scale=-1.0) == INVALID
+    assert f(L, causal=-1) == INVALID
+    assert f(L, ws=0) == WORKSPACE
+    assert f(L, ws_bytes=16) == WORKSPACE
+
+
+def test_interval_output_dtype_and_accumulate_errors(L):
+    assert fwd_iv(L, odt=5) == UNSUPPORTED
+    assert fwd_iv(L, dt=FP32, d=64, odt=BF16) == UNSUPPORTED   # fp32 inputs give fp32 O
+    assert bwd_iv(L, gdt=5) == UNSUPPORTED
+    assert bwd_iv(L, dt=FP32, d=64, gdt=BF16, acc=0) == UNSUPPORTED
+    assert bwd_iv(L, gdt=BF16, acc=1) == INVALID              # accumulation is fp32 only
+    assert bwd_iv(L, acc=2) == INVALID
+    z = [A + (i << 24) for i in range(9)]
+    assert fwd_iv(L, ptrs=(z[0], z[1], z[2], z[1] + 256, z[4])) == INVALID  # o overlaps k
+    p = list(z)
+    p[7] = p[6] + 4096  # dk overlaps dq
+    assert bwd_iv(L, ptrs=p) == INVALID
+
+
+def merge(L, oa=A, la=A + (1 << 24), ob=A + (2 << 24), lb=A + (3 << 24), o=A + (4 << 24),
+          lse=A + (5 << 24), s_q=100, hq=4, d=128, odt=FP32):
+    return L.usp_attn_merge(*(ctypes.c_void_p(x) for x in (oa, la, ob, lb, o, lse)), s_q, hq, d,
+                            odt, None)
+
+
+def test_merge_argument_errors(L):
+    assert merge(L, s_q=0) == INVALID
+    assert merge(L, hq=0) == INVALID
+    assert merge(L, s_q=1 << 22, hq=8, d=128) == INVALID     # 32-bit element count
+    assert merge(L, d=96) == UNSUPPORTED
+    assert merge(L, odt=4) == UNSUPPORTED
+    assert merge(L, oa=0) == NULLP
+    assert merge(L, lse=0) == NULLP
+    assert merge(L, o=A + (4 << 24) + 4) == INVALID          # misaligned
+    assert merge(L, o=A + 1024) == INVALID                    # partly overlaps o_a
+    assert merge(L, o=A, odt=BF16) == INVALID                 # in place needs fp32 O
+    assert merge(L, lse=A + (1 << 24) + 16) == INVALID        # partly overlaps lse_a
+    assert merge(L, o=A + (1 << 24)) == INVALID               # O over lse_a
+
+
 def test_workspace_sizes(L):
     for s in (1, 100, 128, 129, 120000, 131072):
         f = L.usp_attn_fwd_workspace_bytes(s, 4, 1, 128, BF16)
@@ -157,6 +231,14 @@ def test_workspace_sizes(L):
     assert L.usp_attn_fwd_workspace_bytes(512, 4, 2, 64, FP32) == 0
     assert L.usp_attn_bwd_workspace_bytes(512, 4, 2, 64, FP32) == 512 * 4 * 4
     assert L.usp_attn_fwd_workspace_bytes(0, 4, 1, 128, BF16) == 0
+    # interval: key-major Q / dO / D sized by the query rows, K by the keys
+    for s_q, s_k in ((100, 1000), (1000, 100), (512, 512)):
+        b = L.usp_attn_bwd_interval_workspace_bytes(s_q, s_k, 4, 1, 128, BF16)
+        assert b >= 2 * 4 * 128 * s_q * 2 + 128 * s_k * 2 + 4 * s_q * 4
+        assert b < 2 * 4 * 128 * (s_q + 256) * 2 + 128 * (s_k + 256) * 2 + 4 * (s_q + 256) * 4 + 4096
+    assert L.usp_attn_bwd_interval_workspace_bytes(512, 512, 4, 1, 128, BF16) == \
+        L.usp_attn_bwd_workspace_bytes(512, 4, 1, 128, BF16)
+    assert L.usp_attn_bwd_interval_workspace_bytes(300, 700, 4, 2, 64, FP32) == 300 * 4 * 4
 
 
 def test_fast_division_host_side(tmp_path):

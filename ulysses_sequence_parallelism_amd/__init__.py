@@ -29,6 +29,10 @@ __all__ = [
     "usp_attn_fwd",
     "usp_attn_bwd_workspace_bytes",
     "usp_attn_bwd",
+    "usp_attn_fwd_interval",
+    "usp_attn_merge",
+    "usp_attn_bwd_interval_workspace_bytes",
+    "usp_attn_bwd_interval",
     "usp_trace_enable",
     "usp_trace_collect",
     "USP_BF16",
@@ -88,6 +92,17 @@ def lib() -> ctypes.CDLL:
         L.usp_attn_bwd.restype = i32
         L.usp_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, vp, i32,
                                    i32, i32, i32, f32, i32, i32, vp]
+        L.usp_attn_fwd_interval.restype = i32
+        L.usp_attn_fwd_interval.argtypes = [vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64,
+                                            vp, i32, i32, i32, i32, f32, i32, i32, i32, vp]
+        L.usp_attn_merge.restype = i32
+        L.usp_attn_merge.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, vp]
+        L.usp_attn_bwd_interval_workspace_bytes.restype = sz
+        L.usp_attn_bwd_interval_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
+        L.usp_attn_bwd_interval.restype = i32
+        L.usp_attn_bwd_interval.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64,
+                                            i64, i64, i64, vp, i32, i32, i32, i32, f32, i32, i32,
+                                            i32, i32, vp]
         _lib = L
     return _lib
 
@@ -131,6 +146,20 @@ def _contig(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _shapes(fn, **named):
+    """Every tensor must have exactly the shape the C call will assume (the
+    library sees only pointers and sizes)."""
+    for name, (t, shape) in named.items():
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{fn}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _same_dtype(fn, dtype, **named):
+    for name, t in named.items():
+        if t.dtype != dtype:
+            raise ValueError(f"{fn}: {name} is {t.dtype}, expected {dtype}")
+
+
 def usp_pad_pack_seq2head(x: torch.Tensor, p: int, out: torch.Tensor | None = None,
                           stream=None) -> torch.Tensor:
     """x [s_real, H, d] -> y [p, s_pad, H/p, d] (see usp.h)."""
@@ -142,6 +171,9 @@ def usp_pad_pack_seq2head(x: torch.Tensor, p: int, out: torch.Tensor | None = No
             raise UspError("usp_pad_pack_seq2head", -1)
         out = torch.empty((p, s_pad, h // p, d), dtype=x.dtype, device=x.device)
     _contig(out)
+    if p >= 1 and h % p == 0:
+        _shapes("usp_pad_pack_seq2head", out=(out, (p, s_pad, h // p, d)))
+    _same_dtype("usp_pad_pack_seq2head", x.dtype, out=out)
     _check("usp_pad_pack_seq2head",
            lib().usp_pad_pack_seq2head(_ptr(x), _ptr(out), s_real, p, h, d, _dtype(x),
                                        _stream(stream)))
@@ -158,6 +190,8 @@ def usp_unpack_head2seq(y: torch.Tensor, s_real: int, out: torch.Tensor | None =
     if out is None:
         out = torch.empty((s_real, p * hp, d), dtype=y.dtype, device=y.device)
     _contig(out)
+    _shapes("usp_unpack_head2seq", out=(out, (s_real, p * hp, d)))
+    _same_dtype("usp_unpack_head2seq", y.dtype, out=out)
     _check("usp_unpack_head2seq",
            lib().usp_unpack_head2seq(_ptr(y), _ptr(out), s_real, p, p * hp, d, _dtype(y),
                                      _stream(stream)))
@@ -209,6 +243,11 @@ def usp_attn_fwd(q, k, v, s_valid=None, cu_seqlens=None, causal=True, softmax_sc
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((hq, s_pad), dtype=torch.float32, device=q.device)
+    _contig(out, lse)
+    _shapes("usp_attn_fwd", k=(k, (s_pad, hkv, d)), v=(v, (s_pad, hkv, d)), out=(out, q.shape),
+            lse=(lse, (hq, s_pad)))
+    _same_dtype("usp_attn_fwd", q.dtype, k=k, v=v, out=out)
+    _same_dtype("usp_attn_fwd", torch.float32, lse=lse)
     ws = _workspace(usp_attn_fwd_workspace_bytes(s_pad, hq, hkv, d, dt), q.device, workspace)
     _check("usp_attn_fwd", lib().usp_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws),
@@ -230,6 +269,12 @@ def usp_attn_bwd(q, k, v, o, lse, dout, s_valid=None, cu_seqlens=None, causal=Tr
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _contig(dq, dk, dv)
+    kshape = (s_pad, hkv, d)
+    _shapes("usp_attn_bwd", k=(k, kshape), v=(v, kshape), o=(o, q.shape), dout=(dout, q.shape),
+            lse=(lse, (hq, s_pad)), dq=(dq, q.shape), dk=(dk, kshape), dv=(dv, kshape))
+    _same_dtype("usp_attn_bwd", q.dtype, k=k, v=v, o=o, dout=dout, dq=dq, dk=dk, dv=dv)
+    _same_dtype("usp_attn_bwd", torch.float32, lse=lse)
     ws = _workspace(usp_attn_bwd_workspace_bytes(s_pad, hq, hkv, d, dt), q.device, workspace)
     _check("usp_attn_bwd", lib().usp_attn_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
@@ -252,3 +297,109 @@ def usp_trace_collect(max_entries: int = 64) -> list[dict]:
         raise UspError("usp_trace_collect", n)
     return [{"name": buf[i].name.decode(), "launches": int(buf[i].launches),
              "total_ms": float(buf[i].total_ms)} for i in range(n)]
+
+
+def _cu_global(cu_seqlens, extent, device):
+    """Validate document offsets over global positions on the host: they start
+    at 0, never decrease and cover every position the call touches."""
+    if cu_seqlens is None:
+        return None, 0
+    host = torch.as_tensor(cu_seqlens).to("cpu", torch.int64)
+    if host.ndim != 1 or host.numel() < 2 or int(host[0]) != 0 or int(host[-1]) < extent \
+            or bool((host[1:] < host[:-1]).any()):
+        raise UspError("cu_seqlens", -1)
+    return host.to(device=device, dtype=torch.int32), host.numel() - 1
+
+
+def usp_attn_fwd_interval(q, k, v, q_off=0, k_off=0, s_k_valid=None, cu_seqlens=None,
+                          causal=True, softmax_scale=None, out_dtype=torch.float32, out=None,
+                          lse=None, workspace=None, stream=None):
+    """Attention of query rows at global positions q_off + [0, s_q) against keys
+    at k_off + [0, s_k) (see usp.h). q [s_q, hq, d], k and v [s_k, hkv, d].
+    Returns (o [s_q, hq, d] in out_dtype, lse [hq, s_q] fp32); rows without an
+    allowed key get o = 0, lse = -inf."""
+    _contig(q, k, v)
+    s_q, hq, d = q.shape
+    s_k, hkv = k.shape[0], k.shape[1]
+    s_k_valid = s_k if s_k_valid is None else s_k_valid
+    scale = float(d) ** -0.5 if softmax_scale is None else softmax_scale
+    dt = _dtype(q)
+    cu, n_docs = _cu_global(cu_seqlens, max(q_off + s_q, k_off + s_k), q.device)
+    if out is None:
+        out = torch.empty((s_q, hq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((hq, s_q), dtype=torch.float32, device=q.device)
+    _contig(out, lse)
+    _shapes("usp_attn_fwd_interval", v=(v, k.shape), out=(out, q.shape), lse=(lse, (hq, s_q)))
+    _same_dtype("usp_attn_fwd_interval", q.dtype, k=k, v=v)
+    _same_dtype("usp_attn_fwd_interval", torch.float32, lse=lse)
+    ws = _workspace(usp_attn_fwd_workspace_bytes(s_k, hq, hkv, d, dt), q.device, workspace)
+    _check("usp_attn_fwd_interval", lib().usp_attn_fwd_interval(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), s_q, q_off, s_k, k_off, s_k_valid,
+        _ptr(cu), n_docs, hq, hkv, d, scale, int(causal), dt, _dtype(out), _stream(stream)))
+    return out, lse
+
+
+def usp_attn_merge(o_a, lse_a, o_b, lse_b, out=None, lse=None, out_dtype=torch.float32,
+                   stream=None):
+    """Exact log-sum-exp merge of two fp32 partials over disjoint key sets (see
+    usp.h). out / lse may be o_a / lse_a themselves (in-place accumulation).
+    Returns (o [s_q, hq, d] in out's dtype, lse [hq, s_q])."""
+    _contig(o_a, lse_a, o_b, lse_b)
+    s_q, hq, d = o_a.shape
+    if out is None:
+        out = torch.empty((s_q, hq, d), dtype=out_dtype, device=o_a.device)
+    if lse is None:
+        lse = torch.empty((hq, s_q), dtype=torch.float32, device=o_a.device)
+    _contig(out, lse)
+    _shapes("usp_attn_merge", o_b=(o_b, o_a.shape), lse_a=(lse_a, (hq, s_q)),
+            lse_b=(lse_b, (hq, s_q)), out=(out, o_a.shape), lse=(lse, (hq, s_q)))
+    _same_dtype("usp_attn_merge", torch.float32, o_a=o_a, o_b=o_b, lse_a=lse_a, lse_b=lse_b,
+                lse=lse)
+    _check("usp_attn_merge", lib().usp_attn_merge(
+        _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(out), _ptr(lse), s_q, hq, d,
+        _dtype(out), _stream(stream)))
+    return out, lse
+
+
+def usp_attn_bwd_interval_workspace_bytes(s_q: int, s_k: int, hq: int, hkv: int, d: int,
+                                          dtype: int) -> int:
+    return lib().usp_attn_bwd_interval_workspace_bytes(s_q, s_k, hq, hkv, d, dtype)
+
+
+def usp_attn_bwd_interval(q, k, v, o, lse, dout, q_off=0, k_off=0, s_k_valid=None,
+                          cu_seqlens=None, causal=True, softmax_scale=None,
+                          grad_dtype=torch.float32, accumulate=False, dq=None, dk=None, dv=None,
+                          workspace=None, stream=None):
+    """Backward contributions of one (query interval, key interval) pair given
+    the FINAL o and lse of the rows (see usp.h). With accumulate the fp32
+    gradients are added to dq / dk / dv (allocated as zeros when not given).
+    Returns (dq, dk, dv)."""
+    _contig(q, k, v, o, lse, dout)
+    s_q, hq, d = q.shape
+    s_k, hkv = k.shape[0], k.shape[1]
+    s_k_valid = s_k if s_k_valid is None else s_k_valid
+    scale = float(d) ** -0.5 if softmax_scale is None else softmax_scale
+    dt = _dtype(q)
+    cu, n_docs = _cu_global(cu_seqlens, max(q_off + s_q, k_off + s_k), q.device)
+    alloc = torch.zeros if accumulate else torch.empty
+    dq = alloc((s_q, hq, d), dtype=grad_dtype, device=q.device) if dq is None else dq
+    dk = alloc((s_k, hkv, d), dtype=grad_dtype, device=q.device) if dk is None else dk
+    dv = alloc((s_k, hkv, d), dtype=grad_dtype, device=q.device) if dv is None else dv
+    _contig(dq, dk, dv)
+    _shapes("usp_attn_bwd_interval", v=(v, k.shape), o=(o, q.shape), dout=(dout, q.shape),
+            lse=(lse, (hq, s_q)), dq=(dq, q.shape), dk=(dk, k.shape), dv=(dv, k.shape))
+    _same_dtype("usp_attn_bwd_interval", q.dtype, k=k, v=v, o=o, dout=dout)
+    _same_dtype("usp_attn_bwd_interval", torch.float32, lse=lse)
+    gdt = _dtype(dq)
+    if _dtype(dk) != gdt or _dtype(dv) != gdt:
+        raise UspError("usp_attn_bwd_interval", -1)
+    ws = _workspace(usp_attn_bwd_interval_workspace_bytes(s_q, s_k, hq, hkv, d, dt), q.device,
+                    workspace)
+    _check("usp_attn_bwd_interval", lib().usp_attn_bwd_interval(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), s_q, q_off, s_k, k_off,
+        s_k_valid, _ptr(cu), n_docs, hq, hkv, d, scale, int(causal), dt, gdt, int(accumulate),
+        _stream(stream)))
+    return dq, dk, dv

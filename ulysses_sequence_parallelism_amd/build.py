@@ -34,7 +34,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 SOURCES = ["capi.hip", "trace.hip", "permute.hip", "kmajor.hip", "attn_f32.hip", "attn_fwd_bf16.hip",
-           "attn_bwd_bf16.hip"]
+           "attn_bwd_bf16.hip", "merge.hip"]
 
 
 def _compile(src: str, verbose: bool) -> str:

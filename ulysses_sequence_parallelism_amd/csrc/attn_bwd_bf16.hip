@@ -7,6 +7,13 @@
 //     dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO
 // with dK and dV summed over the query heads that share a key/value head.
 //
+// For a query interval against a key interval on global positions (one ring
+// step of Ring / USP attention, or a contiguous context-parallel rank's rows;
+// see the forward) the same kernels give that pair's contributions: with the
+// FINAL O and LSE of the rows, dQ summed over the key intervals and dK, dV
+// summed over the query intervals are the full gradients. fp32 outputs may be
+// accumulated in place for that sum.
+//
 // Design (gfx950): two matrix-core kernels, each with one operand stationary
 // in registers, so neither needs atomics and both are deterministic.
 //   * dK/dV kernel (key-stationary): a workgroup owns 128 keys of one KV head
@@ -48,13 +55,13 @@ constexpr int KP = D + 8;    // row-major tile pitch (elements)
 // D_i = sum_d dO[i][h][d] * O[i][h][d]  (fp32 from the bf16 values)
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const __bf16* __restrict__ o,
                                                          const __bf16* __restrict__ dout,
-                                                         float* __restrict__ dd, int s_pad,
+                                                         float* __restrict__ dd, int s_q,
                                                          int hq, int64_t s_t) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 16 lanes per (row, head)
   const int64_t rh = t >> 4;
   const int part = (int)(t & 15);
   float s = 0.f;
-  const bool live = rh < (int64_t)s_pad * hq;
+  const bool live = rh < (int64_t)s_q * hq;
   if (live) {
     u32x4 a = *reinterpret_cast<const u32x4*>(o + rh * D + part * 8);
     u32x4 b = *reinterpret_cast<const u32x4*>(dout + rh * D + part * 8);
@@ -77,19 +84,50 @@ struct BwdParams {
   const __bf16* k;
   const __bf16* v;
   const __bf16* dout;
-  const __bf16* qt;    // key-major Q   [hq][D][s_t]
-  const __bf16* dot;   // key-major dO  [hq][D][s_t]
-  const __bf16* kt;    // key-major K   [hkv][D][s_t]
-  const float* lse;    // [hq][s_pad]
-  const float* dd;     // [hq][s_t]
-  __bf16* dq;
-  __bf16* dk;
-  __bf16* dv;
-  const int32_t* cu;
-  int64_t s_t;
-  int s_pad, s_valid, n_docs, hq, hkv, causal, n_blocks;
+  const __bf16* qt;    // key-major Q   [hq][D][s_tq]
+  const __bf16* dot;   // key-major dO  [hq][D][s_tq]
+  const __bf16* kt;    // key-major K   [hkv][D][s_tk]
+  const float* lse;    // [hq][s_q]
+  const float* dd;     // [hq][s_tq]
+  void* dq;            // [s_q][hq][D]
+  void* dk;            // [s_k][hkv][D]
+  void* dv;            // [s_k][hkv][D]
+  MaskGeom m;
+  int64_t s_tq, s_tk;
+  int hq, hkv, n_blocks;
+  int grad_f32, accum;  // fp32 gradients; add to the existing contents
   float scale, scale_log2;
 };
+
+// Write 4 x 4 accumulator values (registers 4r..4r+3 of block b go to
+// elements b*32 + r*8 + [0, 4) past p) scaled by f, as bf16, as fp32, or added
+// to fp32.
+__device__ __forceinline__ void store_rows(void* out, int64_t off, const f32x16 (&acc)[4],
+                                           float f, int f32, int accum) {
+  if (f32) {
+    float* p = static_cast<float*>(out) + off;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        f32x4 v4 = {acc[b][4 * r] * f, acc[b][4 * r + 1] * f, acc[b][4 * r + 2] * f,
+                    acc[b][4 * r + 3] * f};
+        f32x4* dst = reinterpret_cast<f32x4*>(p + b * 32 + r * 8);
+        if (accum) v4 += *dst;
+        *dst = v4;
+      }
+  } else {
+    __bf16* p = static_cast<__bf16*>(out) + off;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        u32x2 v2 = {pack_bf16x2(acc[b][4 * r] * f, acc[b][4 * r + 1] * f),
+                    pack_bf16x2(acc[b][4 * r + 2] * f, acc[b][4 * r + 3] * f)};
+        *reinterpret_cast<u32x2*>(p + b * 32 + r * 8) = v2;
+      }
+  }
+}
 
 // ---------------------------------------------------------------------------
 // dK / dV: key-stationary. A workgroup owns 128 keys of one KV head (four
@@ -119,33 +157,30 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = w & 3, role = w >> 2;
   const int hl = lane >> 5, ln = lane & 31;
-  const int s_pad = pr.s_pad, s_valid = pr.s_valid, causal = pr.causal;
+  const int s_q = pr.m.s_q, s_k = pr.m.s_k, s_kv = pr.m.s_kv;
   const int g = pr.hq / pr.hkv;
   const int kvh = blockIdx.y;
   const int j0 = blockIdx.x * 128;
-  const int j1 = min(j0 + 128, s_pad);
+  const int j1 = min(j0 + 128, s_k);
   const int wj0 = j0 + grp * 32;
   const int key = wj0 + ln;
-  const int kc = min(key, s_pad - 1);
+  const int kc = min(key, s_k - 1);
 
-  // this lane's key: rows [rlo, rhi) may see it
-  const DocBounds kb_ = doc_bounds(pr.cu, pr.n_docs, kc, s_pad);
-  const bool key_ok = key < s_valid;
-  const int rlo = max(kb_.lo, causal ? key : 0);
-  const int rhi = kb_.hi;
+  // this lane's key: rows [rlo, rhi) may see it (both ends nondecreasing in
+  // the key)
+  const RowSpan kr = key_rows(pr.m, kc);
+  const bool key_ok = key < s_kv;
+  const int rlo = kr.lo, rhi = kr.hi;
   // workgroup row range and mask-free test
-  const DocBounds dfirst = doc_bounds(pr.cu, pr.n_docs, j0, s_pad);
-  const DocBounds dlast = doc_bounds(pr.cu, pr.n_docs, j1 - 1, s_pad);
-  const int rstart = causal ? j0 : dfirst.lo;
-  const int rend = dlast.hi - 1;
-  const int free_lo = max(dlast.lo, causal ? j1 - 1 : 0);
-  const int free_hi = dfirst.hi - 1;
-  const bool all_keys_valid = j1 - 1 < s_valid;
+  const RowSpan rfirst = key_rows(pr.m, j0), rlast = key_rows(pr.m, j1 - 1);
+  const int rstart = max(rfirst.lo, 0);
+  const int rend = rlast.hi - 1;
+  const int free_lo = rlast.lo, free_hi = rfirst.hi - 1;
+  const bool all_keys_valid = j1 - 1 < s_kv;
   // this key group's row range
-  const int wlast = min(wj0 + 31, s_pad - 1);
-  const bool wave_live = wj0 < s_pad && wj0 < s_valid;
-  const int wr_lo = causal ? wj0 : doc_bounds(pr.cu, pr.n_docs, min(wj0, s_pad - 1), s_pad).lo;
-  const int wr_hi = doc_bounds(pr.cu, pr.n_docs, wlast, s_pad).hi - 1;
+  const bool wave_live = wj0 < s_k && wj0 < s_kv;
+  const int wr_lo = key_rows(pr.m, min(wj0, s_k - 1)).lo;
+  const int wr_hi = key_rows(pr.m, min(wj0 + 31, s_k - 1)).hi - 1;
 
   // stationary fragment (B operand, lane = key): K for role 0, V for role 1
   bf16x8 sreg[8];
@@ -164,7 +199,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
   for (int b = 0; b < 4; ++b) acc[b] = f32x16{};
 
   const int tstart = (rstart / BQ) * BQ;
-  const int ntr = (j0 < s_valid && rend >= rstart) ? (rend - tstart) / BQ + 1 : 0;
+  const int ntr = (j0 < s_kv && rend >= rstart) ? (rend - tstart) / BQ + 1 : 0;
   const int nt = ntr * g;
 
   u32x4 sq[RCH], sdo[RCH], sqt[RCH], sdot[RCH];
@@ -185,19 +220,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
       // rows past the end read the last row instead: every load is
       // unconditional (no wait is forced before the tile is consumed) and
       // such rows are always masked
-      const int i = min(r0 + r, s_pad - 1);
+      const int i = min(r0 + r, s_q - 1);
       const int64_t off = ((int64_t)i * pr.hq + h) * D + c * 8;
       sq[u] = *reinterpret_cast<const u32x4*>(pr.q + off);
       sdo[u] = *reinterpret_cast<const u32x4*>(pr.dout + off);
       const int dr = e / (BQ / 8), c8 = e % (BQ / 8);
-      const int64_t toff = ((int64_t)h * D + dr) * pr.s_t + r0 + c8 * 8;
+      const int64_t toff = ((int64_t)h * D + dr) * pr.s_tq + r0 + c8 * 8;
       sqt[u] = *reinterpret_cast<const u32x4*>(pr.qt + toff);
       sdot[u] = *reinterpret_cast<const u32x4*>(pr.dot + toff);
     }
     {
       // threads [0, BQ) fetch LSE, [BQ, 2 BQ) fetch D, the rest a dummy
-      const int i = min(r0 + (tid % BQ), s_pad - 1);
-      const float* src = tid < BQ ? pr.lse + (int64_t)h * s_pad : pr.dd + (int64_t)h * pr.s_t;
+      const int i = min(r0 + (tid % BQ), s_q - 1);
+      const float* src = tid < BQ ? pr.lse + (int64_t)h * s_q : pr.dd + (int64_t)h * pr.s_tq;
       sld = src[i];
     }
   };
@@ -335,18 +370,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
     __syncthreads();
   }
 
-  if (key < s_pad) {
-    const float f = role == 0 ? 1.f : pr.scale;
-    __bf16* op = (role == 0 ? pr.dv : pr.dk) + ((int64_t)key * pr.hkv + kvh) * D + hl * 4;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        u32x2 v2 = {pack_bf16x2(acc[b][4 * r] * f, acc[b][4 * r + 1] * f),
-                    pack_bf16x2(acc[b][4 * r + 2] * f, acc[b][4 * r + 3] * f)};
-        *reinterpret_cast<u32x2*>(op + b * 32 + r * 8) = v2;
-      }
-  }
+  if (key < s_k)
+    store_rows(role == 0 ? pr.dv : pr.dk, ((int64_t)key * pr.hkv + kvh) * D + hl * 4, acc,
+               role == 0 ? 1.f : pr.scale, pr.grad_f32, pr.accum);
 }
 
 // ---------------------------------------------------------------------------
@@ -365,32 +391,26 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hl = lane >> 5, ln = lane & 31;
-  const int s_pad = pr.s_pad, s_valid = pr.s_valid, causal = pr.causal;
+  const int s_q = pr.m.s_q, s_k = pr.m.s_k;
   const int g = pr.hq / pr.hkv;
   const int chunks = g / HG;
   const int kvh = blockIdx.y / chunks, hc = blockIdx.y % chunks;
   const int head = kvh * g + hc * HG + (w % HG);
   const int qb = pr.n_blocks - 1 - (int)blockIdx.x;
   const int q0 = qb * QROWS;
-  const int q1 = min(q0 + QROWS, s_pad);
+  const int q1 = min(q0 + QROWS, s_q);
   const int wq0 = q0 + (w / HG) * 32;
   const int qi = wq0 + ln;
-  const bool row_ok = qi < s_pad;
-  const int qc = row_ok ? qi : s_pad - 1;
+  const bool row_ok = qi < s_q;
+  const int qc = row_ok ? qi : s_q - 1;
 
-  const DocBounds db = doc_bounds(pr.cu, pr.n_docs, qc, s_pad);
-  const int lo = db.lo;
-  const int hi = causal ? min(qc, s_valid - 1) : min(db.hi, s_valid) - 1;
-  const DocBounds dfirst = doc_bounds(pr.cu, pr.n_docs, q0, s_pad);
-  const DocBounds dlast = doc_bounds(pr.cu, pr.n_docs, q1 - 1, s_pad);
-  const int kmin = dfirst.lo;
-  const int kmax = causal ? min(q1 - 1, s_valid - 1) : min(dlast.hi, s_valid) - 1;
-  const int free_lo = dlast.lo;
-  const int free_hi = causal ? min(q0, s_valid - 1) : min(dfirst.hi, s_valid) - 1;
-  const int wlast = min(wq0 + 31, s_pad - 1);
-  const int wkmin = doc_bounds(pr.cu, pr.n_docs, min(wq0, s_pad - 1), s_pad).lo;
-  const int wkmax = causal ? min(wlast, s_valid - 1)
-                           : min(doc_bounds(pr.cu, pr.n_docs, wlast, s_pad).hi, s_valid) - 1;
+  const KeyRange kr = row_keys(pr.m, qc);
+  const int lo = kr.lo, hi = kr.hi;
+  const KeyRange kfirst = row_keys(pr.m, q0), klast = row_keys(pr.m, q1 - 1);
+  const int kmin = kfirst.lo, kmax = klast.hi;
+  const int free_lo = klast.lo, free_hi = kfirst.hi;
+  const int wkmin = row_keys(pr.m, min(wq0, s_q - 1)).lo;
+  const int wkmax = row_keys(pr.m, min(wq0 + 31, s_q - 1)).hi;
 
   bf16x8 qreg[8], doreg[8];
   {
@@ -401,8 +421,8 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
       doreg[kk] = *reinterpret_cast<const bf16x8*>(pr.dout + off + kk * 16);
     }
   }
-  const float lse2 = pr.lse[(int64_t)head * s_pad + qc] * kLog2e;
-  const float drow = pr.dd[(int64_t)head * pr.s_t + qc];
+  const float lse2 = pr.lse[(int64_t)head * s_q + qc] * kLog2e;
+  const float drow = pr.dd[(int64_t)head * pr.s_tq + qc];
   // retire the stationary loads before the loop (see the dK/dV kernel)
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -420,12 +440,12 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
       const int e = tid + 256 * u;
       const int r = e >> 4, c = e & 15;
       // keys past the end read the last key (always masked): unconditional loads
-      const int j = min(t0 + r, s_pad - 1);
+      const int j = min(t0 + r, s_k - 1);
       const int64_t off = ((int64_t)j * pr.hkv + kvh) * D + c * 8;
       sk[u] = *reinterpret_cast<const u32x4*>(pr.k + off);
       sv[u] = *reinterpret_cast<const u32x4*>(pr.v + off);
       const int dr = e / (BN / 8), c8 = e % (BN / 8);
-      skt[u] = *reinterpret_cast<const u32x4*>(pr.kt + ((int64_t)kvh * D + dr) * pr.s_t + t0 + c8 * 8);
+      skt[u] = *reinterpret_cast<const u32x4*>(pr.kt + ((int64_t)kvh * D + dr) * pr.s_tk + t0 + c8 * 8);
     }
   };
   auto store_tile = [&](int buf) {
@@ -522,17 +542,9 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
     __syncthreads();
   }
 
-  if (row_ok) {
-    __bf16* op = pr.dq + ((int64_t)qi * pr.hq + head) * D + hl * 4;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        u32x2 v2 = {pack_bf16x2(dqa[b][4 * r] * pr.scale, dqa[b][4 * r + 1] * pr.scale),
-                    pack_bf16x2(dqa[b][4 * r + 2] * pr.scale, dqa[b][4 * r + 3] * pr.scale)};
-        *reinterpret_cast<u32x2*>(op + b * 32 + r * 8) = v2;
-      }
-  }
+  if (row_ok)
+    store_rows(pr.dq, ((int64_t)qi * pr.hq + head) * D + hl * 4, dqa, pr.scale, pr.grad_f32,
+               pr.accum);
 }
 
 constexpr int kDqKeys = DQ_KEYS;     // keys per dQ tile
@@ -542,7 +554,7 @@ template <int HG>
 int launch_dq(const BwdParams& p, int g, hipStream_t stream) {
   constexpr int QROWS = 32 * (4 / HG);
   BwdParams pr = p;
-  pr.n_blocks = (p.s_pad + QROWS - 1) / QROWS;
+  pr.n_blocks = (p.m.s_q + QROWS - 1) / QROWS;
   dim3 grid((unsigned)pr.n_blocks, (unsigned)(p.hkv * (g / HG)));
   TraceScope ts("attn_bwd_dq_bf16", stream);
   hipLaunchKernelGGL((bwd_dq_kernel<HG, kDqKeys>), grid, dim3(256), 0, stream, pr);
@@ -553,32 +565,32 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
-size_t attn_bwd_bf16_workspace(int64_t s_pad, int hq, int hkv, int d) {
-  const size_t s_t = (size_t)kmajor_len(s_pad);
-  return align256((size_t)hq * d * s_t * 2) * 2 + align256((size_t)hkv * d * s_t * 2) +
-         align256((size_t)hq * s_t * 4);
+size_t attn_bwd_bf16_workspace(int64_t s_q, int64_t s_k, int hq, int hkv, int d) {
+  const size_t s_tq = (size_t)kmajor_len(s_q), s_tk = (size_t)kmajor_len(s_k);
+  return align256((size_t)hq * d * s_tq * 2) * 2 + align256((size_t)hkv * d * s_tk * 2) +
+         align256((size_t)hq * s_tq * 4);
 }
 
 int attn_bwd_bf16(const AttnArgs& a) {
-  const int64_t s_t = kmajor_len(a.s_pad);
+  const int64_t s_tq = kmajor_len(a.s_q), s_tk = kmajor_len(a.s_k);
   char* ws = static_cast<char*>(a.workspace);
-  const size_t qt_bytes = align256((size_t)a.hq * D * s_t * 2);
-  const size_t kt_bytes = align256((size_t)a.hkv * D * s_t * 2);
+  const size_t qt_bytes = align256((size_t)a.hq * D * s_tq * 2);
+  const size_t kt_bytes = align256((size_t)a.hkv * D * s_tk * 2);
   __bf16* qt = reinterpret_cast<__bf16*>(ws);
   __bf16* dot = reinterpret_cast<__bf16*>(ws + qt_bytes);
   __bf16* kt = reinterpret_cast<__bf16*>(ws + 2 * qt_bytes);
   float* dd = reinterpret_cast<float*>(ws + 2 * qt_bytes + kt_bytes);
 
-  int rc = kmajor_launch(a.q, qt, a.s_pad, a.hq, s_t, a.stream, "attn_bwd_kmajor");
-  if (rc == USP_OK) rc = kmajor_launch(a.dout, dot, a.s_pad, a.hq, s_t, a.stream, "attn_bwd_kmajor");
-  if (rc == USP_OK) rc = kmajor_launch(a.k, kt, a.s_pad, a.hkv, s_t, a.stream, "attn_bwd_kmajor");
+  int rc = kmajor_launch(a.q, qt, a.s_q, a.hq, s_tq, a.stream, "attn_bwd_kmajor");
+  if (rc == USP_OK) rc = kmajor_launch(a.dout, dot, a.s_q, a.hq, s_tq, a.stream, "attn_bwd_kmajor");
+  if (rc == USP_OK) rc = kmajor_launch(a.k, kt, a.s_k, a.hkv, s_tk, a.stream, "attn_bwd_kmajor");
   if (rc != USP_OK) return rc;
   {
-    const int64_t n = a.s_pad * a.hq * 16;
+    const int64_t n = a.s_q * a.hq * 16;
     TraceScope ts("attn_bwd_rowdot_bf16", a.stream);
     hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, a.stream,
                        static_cast<const __bf16*>(a.o), static_cast<const __bf16*>(a.dout), dd,
-                       (int)a.s_pad, a.hq, s_t);
+                       (int)a.s_q, a.hq, s_tq);
     if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
   }
   BwdParams p{};
@@ -591,21 +603,20 @@ int attn_bwd_bf16(const AttnArgs& a) {
   p.kt = kt;
   p.lse = a.lse;
   p.dd = dd;
-  p.dq = static_cast<__bf16*>(a.dq);
-  p.dk = static_cast<__bf16*>(a.dk);
-  p.dv = static_cast<__bf16*>(a.dv);
-  p.cu = a.cu;
-  p.s_t = s_t;
-  p.s_pad = (int)a.s_pad;
-  p.s_valid = (int)a.s_valid;
-  p.n_docs = a.n_docs;
+  p.dq = a.dq;
+  p.dk = a.dk;
+  p.dv = a.dv;
+  p.m = mask_geom(a);
+  p.s_tq = s_tq;
+  p.s_tk = s_tk;
   p.hq = a.hq;
   p.hkv = a.hkv;
-  p.causal = a.causal;
+  p.grad_f32 = a.out_f32;
+  p.accum = a.accumulate;
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
   {
-    dim3 grid((unsigned)((a.s_pad + 127) / 128), (unsigned)a.hkv);
+    dim3 grid((unsigned)((a.s_k + 127) / 128), (unsigned)a.hkv);
     TraceScope ts("attn_bwd_dkdv_bf16", a.stream);
     hipLaunchKernelGGL((bwd_dkdv_kernel<kDkdvRows>), grid, dim3(512), 0, a.stream, p);
     if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;

@@ -8,6 +8,16 @@
 // (packed documents: "GLM-5.2 131k context parallelism", Purpose). The kernel
 // returns O and the natural-log LSE of every row.
 //
+// The same kernel serves a query interval against a key interval on global
+// positions (rows at q_off + i, keys at k_off + j, the causal test and the
+// documents taken on those positions): the partial (O, LSE) of one ring step
+// of Ring / USP attention, merged exactly afterwards (the ring degree of USP:
+// "feat(dspark)", Accuracy Test; "[trainer] feat: support sequence parallel",
+// review overview, the (dp, ring, ulysses) mesh), and a contiguous
+// context-parallel rank's query rows against the whole sequence with a causal
+// offset and global document offsets ("GLM-5.2 131k context parallelism",
+// Purpose). O may be written in fp32 for the merge.
+//
 // Design (gfx950):
 //   * Workgroup = 8 waves that share one KV head: HG query heads of the group
 //     times 8/HG blocks of 32 query rows. Each staged K/V tile feeds every
@@ -56,11 +66,12 @@ struct FwdParams {
   const __bf16* q;
   const __bf16* k;
   const __bf16* vt;   // key-major V: [hkv][D][s_t], 16-chunk reordered
-  __bf16* o;
-  float* lse;
-  const int32_t* cu;
+  __bf16* o;          // [s_q][hq][D], or NULL when o32 is set
+  float* o32;         // fp32 O instead of bf16 (NULL otherwise)
+  float* lse;         // [hq][s_q]
+  MaskGeom m;
   int64_t s_t;
-  int s_pad, s_valid, n_docs, hq, hkv, causal, n_qblocks;
+  int hq, hkv, n_qblocks;
   float scale_log2;   // softmax scale * log2(e)
 };
 
@@ -79,29 +90,24 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
   const int head = kvh * g + hc * HG + (w % HG);
   const int qb = pr.n_qblocks - 1 - (int)blockIdx.x;  // heaviest first
   const int q0 = qb * QROWS;
-  const int q1 = min(q0 + QROWS, pr.s_pad);
+  const int s_q = pr.m.s_q, s_k = pr.m.s_k;
+  const int q1 = min(q0 + QROWS, s_q);
   const int wq0 = q0 + (w / HG) * 32;
   const int qi = wq0 + ln;
-  const bool row_ok = qi < pr.s_pad;
-  const int qc = row_ok ? qi : pr.s_pad - 1;
-  const int s_pad = pr.s_pad, s_valid = pr.s_valid, causal = pr.causal;
+  const bool row_ok = qi < s_q;
+  const int qc = row_ok ? qi : s_q - 1;
 
   // this lane's allowed keys [lo, hi]
-  const DocBounds db = doc_bounds(pr.cu, pr.n_docs, qc, s_pad);
-  const int lo = db.lo;
-  const int hi = causal ? min(qc, s_valid - 1) : min(db.hi, s_valid) - 1;
-  // workgroup key range and the range that needs no mask
-  const DocBounds dfirst = doc_bounds(pr.cu, pr.n_docs, q0, s_pad);
-  const DocBounds dlast = doc_bounds(pr.cu, pr.n_docs, q1 - 1, s_pad);
-  const int kmin = dfirst.lo;
-  const int kmax = causal ? min(q1 - 1, s_valid - 1) : min(dlast.hi, s_valid) - 1;
-  const int free_lo = dlast.lo;
-  const int free_hi = causal ? min(q0, s_valid - 1) : min(dfirst.hi, s_valid) - 1;
+  const KeyRange kr = row_keys(pr.m, qc);
+  const int lo = kr.lo, hi = kr.hi;
+  // workgroup key range and the range that needs no mask (both ends of a
+  // row's range are nondecreasing in the row)
+  const KeyRange kfirst = row_keys(pr.m, q0), klast = row_keys(pr.m, q1 - 1);
+  const int kmin = kfirst.lo, kmax = klast.hi;
+  const int free_lo = klast.lo, free_hi = kfirst.hi;
   // this wave's key range (waves of one workgroup may cover different rows)
-  const int wlast = min(wq0 + 31, s_pad - 1);
-  const int wkmin = doc_bounds(pr.cu, pr.n_docs, min(wq0, s_pad - 1), s_pad).lo;
-  const int wkmax = causal ? min(wlast, s_valid - 1)
-                           : min(doc_bounds(pr.cu, pr.n_docs, wlast, s_pad).hi, s_valid) - 1;
+  const int wkmin = row_keys(pr.m, min(wq0, s_q - 1)).lo;
+  const int wkmax = row_keys(pr.m, min(wq0 + 31, s_q - 1)).hi;
 
   // Q fragment: B operand of S^T = K Q^T, lane holds Q[qc][16kk + 8hl .. +7]
   bf16x8 qreg[8];
@@ -135,7 +141,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
     for (int u = 0; u < 2; ++u) {
       const int r = (tid >> 4) + 32 * u, c = tid & 15;
       // keys past the end read the last key (always masked): unconditional loads
-      const int j = min(t0 + r, s_pad - 1);
+      const int j = min(t0 + r, s_k - 1);
       stk[u] = *reinterpret_cast<const u32x4*>(pr.k + ((int64_t)j * pr.hkv + kvh) * D + c * 8);
     }
   };
@@ -288,17 +294,28 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
   const float l_tot = half_swap_sum(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    __bf16* op = pr.o + ((int64_t)qi * pr.hq + head) * D + hl * 4;
+    const int64_t ob = ((int64_t)qi * pr.hq + head) * D + hl * 4;
+    if (pr.o32 != nullptr) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        u32x2 v2 = {pack_bf16x2(oacc[b][4 * r] * inv, oacc[b][4 * r + 1] * inv),
-                    pack_bf16x2(oacc[b][4 * r + 2] * inv, oacc[b][4 * r + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + b * 32 + r * 8) = v2;
-      }
+        for (int r = 0; r < 4; ++r) {
+          f32x4 v4 = {oacc[b][4 * r] * inv, oacc[b][4 * r + 1] * inv, oacc[b][4 * r + 2] * inv,
+                      oacc[b][4 * r + 3] * inv};
+          *reinterpret_cast<f32x4*>(pr.o32 + ob + b * 32 + r * 8) = v4;
+        }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          u32x2 v2 = {pack_bf16x2(oacc[b][4 * r] * inv, oacc[b][4 * r + 1] * inv),
+                      pack_bf16x2(oacc[b][4 * r + 2] * inv, oacc[b][4 * r + 3] * inv)};
+          *reinterpret_cast<u32x2*>(pr.o + ob + b * 32 + r * 8) = v2;
+        }
+    }
     if (hl == 0)
-      pr.lse[(int64_t)head * s_pad + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      pr.lse[(int64_t)head * s_q + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -306,7 +323,7 @@ template <int HG>
 int launch_fwd(const FwdParams& p, int g, int hkv, hipStream_t stream) {
   constexpr int QROWS = 32 * (8 / HG);
   FwdParams pr = p;
-  pr.n_qblocks = (p.s_pad + QROWS - 1) / QROWS;
+  pr.n_qblocks = (p.m.s_q + QROWS - 1) / QROWS;
   dim3 grid((unsigned)pr.n_qblocks, (unsigned)(hkv * (g / HG)));
   TraceScope ts("attn_fwd_bf16", stream);
   hipLaunchKernelGGL((fwd_bf16_kernel<HG>), grid, dim3(512), 0, stream, pr);
@@ -315,28 +332,25 @@ int launch_fwd(const FwdParams& p, int g, int hkv, hipStream_t stream) {
 
 }  // namespace
 
-size_t attn_fwd_bf16_workspace(int64_t s_pad, int, int hkv, int d) {
-  return (size_t)hkv * d * kmajor_len(s_pad) * 2;
+size_t attn_fwd_bf16_workspace(int64_t s_k, int, int hkv, int d) {
+  return (size_t)hkv * d * kmajor_len(s_k) * 2;
 }
 
 int attn_fwd_bf16(const AttnArgs& a) {
-  const int64_t s_t = kmajor_len(a.s_pad);
-  int rc = kmajor_launch(a.v, a.workspace, a.s_pad, a.hkv, s_t, a.stream, "attn_fwd_kmajor_v");
+  const int64_t s_t = kmajor_len(a.s_k);
+  int rc = kmajor_launch(a.v, a.workspace, a.s_k, a.hkv, s_t, a.stream, "attn_fwd_kmajor_v");
   if (rc != USP_OK) return rc;
   FwdParams p{};
   p.q = static_cast<const __bf16*>(a.q);
   p.k = static_cast<const __bf16*>(a.k);
   p.vt = static_cast<const __bf16*>(a.workspace);
-  p.o = static_cast<__bf16*>(a.o_out);
+  p.o = a.out_f32 ? nullptr : static_cast<__bf16*>(a.o_out);
+  p.o32 = a.out_f32 ? static_cast<float*>(a.o_out) : nullptr;
   p.lse = a.lse_out;
-  p.cu = a.cu;
+  p.m = mask_geom(a);
   p.s_t = s_t;
-  p.s_pad = (int)a.s_pad;
-  p.s_valid = (int)a.s_valid;
-  p.n_docs = a.n_docs;
   p.hq = a.hq;
   p.hkv = a.hkv;
-  p.causal = a.causal;
   p.scale_log2 = a.scale * kLog2e;
   const int g = a.hq / a.hkv;
   if (g % 4 == 0) return launch_fwd<4>(p, g, a.hkv, a.stream);

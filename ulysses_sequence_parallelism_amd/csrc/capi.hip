@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 100;
+constexpr int kAbiVersion = 110;
 
 size_t elem_bytes(int dtype) { return dtype == USP_BF16 ? 2 : 4; }
 
@@ -42,19 +42,126 @@ int check_permute(const void* src, const void* dst, int64_t s_real, int p, int h
   return USP_OK;
 }
 
-int check_attn(int64_t s_pad, int64_t s_valid, const int32_t* cu, int n_docs, int hq, int hkv,
-               int d, float scale, int causal, int dtype) {
+constexpr int64_t kMaxPos = (int64_t)1 << 30;  // global positions are 32-bit in the kernels
+
+int check_heads(int hq, int hkv, int d, float scale, int causal, int dtype) {
   if (dtype != USP_BF16 && dtype != USP_FP32) return USP_ERR_UNSUPPORTED;
-  if (s_pad < 1 || s_pad >= (int64_t)1 << 30) return USP_ERR_INVALID;
-  if (s_valid < 1 || s_valid > s_pad) return USP_ERR_INVALID;
   if (hq < 1 || hkv < 1 || hq % hkv != 0) return USP_ERR_INVALID;
   if (!(scale > 0.f) || !isfinite(scale)) return USP_ERR_INVALID;
   if (causal != 0 && causal != 1) return USP_ERR_INVALID;
-  if (cu != nullptr && (n_docs < 1 || s_valid != s_pad)) return USP_ERR_INVALID;
   if (dtype == USP_BF16 && d != 128) return USP_ERR_UNSUPPORTED;
   if (dtype == USP_FP32 && d != 64 && d != 128) return USP_ERR_UNSUPPORTED;
+  return USP_OK;
+}
+
+int check_attn(int64_t s_pad, int64_t s_valid, const int32_t* cu, int n_docs, int hq, int hkv,
+               int d, float scale, int causal, int dtype) {
+  int rc = check_heads(hq, hkv, d, scale, causal, dtype);
+  if (rc != USP_OK) return rc;
+  if (s_pad < 1 || s_pad >= kMaxPos) return USP_ERR_INVALID;
+  if (s_valid < 1 || s_valid > s_pad) return USP_ERR_INVALID;
+  if (cu != nullptr && (n_docs < 1 || s_valid != s_pad)) return USP_ERR_INVALID;
   if ((double)s_pad * hq * d >= 9.0e15) return USP_ERR_INVALID;
   return USP_OK;
+}
+
+int check_interval(int64_t s_q, int64_t q_off, int64_t s_k, int64_t k_off, int64_t s_k_valid,
+                   const int32_t* cu, int n_docs, int hq, int hkv, int d, float scale, int causal,
+                   int dtype) {
+  int rc = check_heads(hq, hkv, d, scale, causal, dtype);
+  if (rc != USP_OK) return rc;
+  if (s_q < 1 || s_k < 1 || q_off < 0 || k_off < 0) return USP_ERR_INVALID;
+  if (q_off + s_q >= kMaxPos || k_off + s_k >= kMaxPos) return USP_ERR_INVALID;
+  if (s_k_valid < 0 || s_k_valid > s_k) return USP_ERR_INVALID;
+  if (cu != nullptr && n_docs < 1) return USP_ERR_INVALID;
+  if ((double)(s_q > s_k ? s_q : s_k) * hq * d >= 9.0e15) return USP_ERR_INVALID;
+  return USP_OK;
+}
+
+// The attention call with both ends as intervals: every entry point lands here
+// after its own checks.
+usp::AttnArgs interval_args(int64_t s_q, int64_t q_off, int64_t s_k, int64_t k_off,
+                            int64_t s_k_valid, const int32_t* cu, int n_docs, int hq, int hkv,
+                            int d, float scale, int causal, void* stream) {
+  usp::AttnArgs a{};
+  a.s_q = s_q; a.q_off = q_off; a.s_k = s_k; a.k_off = k_off; a.s_kv = s_k_valid;
+  a.lim = q_off + s_q > k_off + s_k ? q_off + s_q : k_off + s_k;
+  a.cu = cu; a.n_docs = n_docs;
+  a.hq = hq; a.hkv = hkv; a.d = d; a.scale = scale; a.causal = causal;
+  a.stream = static_cast<hipStream_t>(stream);
+  return a;
+}
+
+int fwd_checked(const void* q, const void* k, const void* v, void* o, float* lse,
+                void* workspace, size_t workspace_bytes, int64_t s_q, int64_t q_off, int64_t s_k,
+                int64_t k_off, int64_t s_k_valid, const int32_t* cu, int n_docs, int hq, int hkv,
+                int d, float scale, int causal, int dtype, int o_dtype, void* stream) {
+  if (o_dtype != USP_BF16 && o_dtype != USP_FP32) return USP_ERR_UNSUPPORTED;
+  if (dtype == USP_FP32 && o_dtype != USP_FP32) return USP_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o || !lse) return USP_ERR_NULL;
+  const void* ptrs[] = {q, k, v, o, lse};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return USP_ERR_INVALID;
+  if (cu && (reinterpret_cast<uintptr_t>(cu) & 3u)) return USP_ERR_INVALID;
+  const size_t es = elem_bytes(dtype);
+  const size_t qb = (size_t)s_q * hq * d * es, kb = (size_t)s_k * hkv * d * es;
+  const size_t ob = (size_t)s_q * hq * d * elem_bytes(o_dtype);
+  const size_t lb = (size_t)s_q * hq * sizeof(float);
+  const size_t need = usp_attn_fwd_workspace_bytes(s_k, hq, hkv, d, dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return USP_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return USP_ERR_INVALID;
+  const Span ins[] = {{q, qb}, {k, kb}, {v, kb}};
+  const Span outs[] = {{o, ob}, {lse, lb}, {workspace, need}};
+  for (const Span& a : outs) {
+    for (const Span& b : ins)
+      if (overlap(a, b)) return USP_ERR_INVALID;
+  }
+  if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2]))
+    return USP_ERR_INVALID;
+  usp::AttnArgs a = interval_args(s_q, q_off, s_k, k_off, s_k_valid, cu, n_docs, hq, hkv, d,
+                                  scale, causal, stream);
+  a.q = q; a.k = k; a.v = v;
+  a.o_out = o; a.lse_out = lse; a.workspace = workspace;
+  a.out_f32 = o_dtype == USP_FP32;
+  return dtype == USP_BF16 ? usp::attn_fwd_bf16(a) : usp::attn_fwd_f32(a);
+}
+
+int bwd_checked(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, int64_t s_q, int64_t q_off, int64_t s_k, int64_t k_off,
+                int64_t s_k_valid, const int32_t* cu, int n_docs, int hq, int hkv, int d,
+                float scale, int causal, int dtype, int grad_dtype, int accumulate, void* stream) {
+  if (grad_dtype != USP_BF16 && grad_dtype != USP_FP32) return USP_ERR_UNSUPPORTED;
+  if (dtype == USP_FP32 && grad_dtype != USP_FP32) return USP_ERR_UNSUPPORTED;
+  if (accumulate != 0 && accumulate != 1) return USP_ERR_INVALID;
+  if (accumulate && grad_dtype != USP_FP32) return USP_ERR_INVALID;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return USP_ERR_NULL;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return USP_ERR_INVALID;
+  if (cu && (reinterpret_cast<uintptr_t>(cu) & 3u)) return USP_ERR_INVALID;
+  const size_t es = elem_bytes(dtype), gs = elem_bytes(grad_dtype);
+  const size_t qb = (size_t)s_q * hq * d * es, kb = (size_t)s_k * hkv * d * es;
+  const size_t gqb = (size_t)s_q * hq * d * gs, gkb = (size_t)s_k * hkv * d * gs;
+  const size_t lb = (size_t)s_q * hq * sizeof(float);
+  const size_t need = usp_attn_bwd_interval_workspace_bytes(s_q, s_k, hq, hkv, d, dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return USP_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return USP_ERR_INVALID;
+  const Span ins[] = {{q, qb}, {k, kb}, {v, kb}, {o, qb}, {lse, lb}, {dout, qb}};
+  const Span outs[] = {{dq, gqb}, {dk, gkb}, {dv, gkb}, {workspace, need}};
+  for (const Span& a : outs)
+    for (const Span& b : ins)
+      if (overlap(a, b)) return USP_ERR_INVALID;
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return USP_ERR_INVALID;
+  usp::AttnArgs a = interval_args(s_q, q_off, s_k, k_off, s_k_valid, cu, n_docs, hq, hkv, d,
+                                  scale, causal, stream);
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.workspace = workspace;
+  a.out_f32 = grad_dtype == USP_FP32;
+  a.accumulate = accumulate;
+  return dtype == USP_BF16 ? usp::attn_bwd_bf16(a) : usp::attn_bwd_f32(a);
 }
 
 }  // namespace
@@ -116,10 +223,15 @@ size_t usp_attn_fwd_workspace_bytes(int64_t s_pad, int hq, int hkv, int d, int d
   return 0;
 }
 
+size_t usp_attn_bwd_interval_workspace_bytes(int64_t s_q, int64_t s_k, int hq, int hkv, int d,
+                                             int dtype) {
+  if (s_q < 1 || s_k < 1 || hq < 1 || hkv < 1 || d < 1) return 0;
+  if (dtype == USP_BF16) return usp::attn_bwd_bf16_workspace(s_q, s_k, hq, hkv, d);
+  return usp::attn_bwd_f32_workspace(s_q, hq, hkv, d);
+}
+
 size_t usp_attn_bwd_workspace_bytes(int64_t s_pad, int hq, int hkv, int d, int dtype) {
-  if (s_pad < 1 || hq < 1 || hkv < 1 || d < 1) return 0;
-  if (dtype == USP_BF16) return usp::attn_bwd_bf16_workspace(s_pad, hq, hkv, d);
-  return usp::attn_bwd_f32_workspace(s_pad, hq, hkv, d);
+  return usp_attn_bwd_interval_workspace_bytes(s_pad, s_pad, hq, hkv, d, dtype);
 }
 
 int usp_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -128,32 +240,8 @@ int usp_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  float softmax_scale, int causal, int dtype, void* stream) {
   int rc = check_attn(s_pad, s_valid, cu_seqlens, n_docs, hq, hkv, d, softmax_scale, causal, dtype);
   if (rc != USP_OK) return rc;
-  if (!q || !k || !v || !o || !lse) return USP_ERR_NULL;
-  const void* ptrs[] = {q, k, v, o, lse};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return USP_ERR_INVALID;
-  if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return USP_ERR_INVALID;
-  const size_t es = elem_bytes(dtype);
-  const size_t qb = (size_t)s_pad * hq * d * es, kb = (size_t)s_pad * hkv * d * es;
-  const size_t lb = (size_t)s_pad * hq * sizeof(float);
-  const size_t need = usp_attn_fwd_workspace_bytes(s_pad, hq, hkv, d, dtype);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return USP_ERR_WORKSPACE;
-  if (need > 0 && !aligned16(workspace)) return USP_ERR_INVALID;
-  const Span ins[] = {{q, qb}, {k, kb}, {v, kb}};
-  const Span outs[] = {{o, qb}, {lse, lb}, {workspace, need}};
-  for (const Span& a : outs) {
-    for (const Span& b : ins)
-      if (overlap(a, b)) return USP_ERR_INVALID;
-  }
-  if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2]))
-    return USP_ERR_INVALID;
-  usp::AttnArgs a{};
-  a.q = q; a.k = k; a.v = v;
-  a.o_out = o; a.lse_out = lse; a.workspace = workspace;
-  a.s_pad = s_pad; a.s_valid = s_valid; a.cu = cu_seqlens; a.n_docs = n_docs;
-  a.hq = hq; a.hkv = hkv; a.d = d; a.scale = softmax_scale; a.causal = causal;
-  a.stream = static_cast<hipStream_t>(stream);
-  return dtype == USP_BF16 ? usp::attn_fwd_bf16(a) : usp::attn_fwd_f32(a);
+  return fwd_checked(q, k, v, o, lse, workspace, workspace_bytes, s_pad, 0, s_pad, 0, s_valid,
+                     cu_seqlens, n_docs, hq, hkv, d, softmax_scale, causal, dtype, dtype, stream);
 }
 
 int usp_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -163,32 +251,63 @@ int usp_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
                  float softmax_scale, int causal, int dtype, void* stream) {
   int rc = check_attn(s_pad, s_valid, cu_seqlens, n_docs, hq, hkv, d, softmax_scale, causal, dtype);
   if (rc != USP_OK) return rc;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return USP_ERR_NULL;
-  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  return bwd_checked(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, s_pad, 0,
+                     s_pad, 0, s_valid, cu_seqlens, n_docs, hq, hkv, d, softmax_scale, causal,
+                     dtype, dtype, 0, stream);
+}
+
+int usp_attn_fwd_interval(const void* q, const void* k, const void* v, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, int64_t s_q, int64_t q_off,
+                          int64_t s_k, int64_t k_off, int64_t s_k_valid,
+                          const int32_t* cu_seqlens, int n_docs, int hq, int hkv, int d,
+                          float softmax_scale, int causal, int dtype, int o_dtype, void* stream) {
+  int rc = check_interval(s_q, q_off, s_k, k_off, s_k_valid, cu_seqlens, n_docs, hq, hkv, d,
+                          softmax_scale, causal, dtype);
+  if (rc != USP_OK) return rc;
+  return fwd_checked(q, k, v, o, lse, workspace, workspace_bytes, s_q, q_off, s_k, k_off,
+                     s_k_valid, cu_seqlens, n_docs, hq, hkv, d, softmax_scale, causal, dtype,
+                     o_dtype, stream);
+}
+
+int usp_attn_bwd_interval(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes, int64_t s_q, int64_t q_off,
+                          int64_t s_k, int64_t k_off, int64_t s_k_valid,
+                          const int32_t* cu_seqlens, int n_docs, int hq, int hkv, int d,
+                          float softmax_scale, int causal, int dtype, int grad_dtype,
+                          int accumulate, void* stream) {
+  int rc = check_interval(s_q, q_off, s_k, k_off, s_k_valid, cu_seqlens, n_docs, hq, hkv, d,
+                          softmax_scale, causal, dtype);
+  if (rc != USP_OK) return rc;
+  return bwd_checked(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, s_q, q_off,
+                     s_k, k_off, s_k_valid, cu_seqlens, n_docs, hq, hkv, d, softmax_scale, causal,
+                     dtype, grad_dtype, accumulate, stream);
+}
+
+int usp_attn_merge(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
+                   void* o, float* lse, int64_t s_q, int hq, int d, int o_dtype, void* stream) {
+  if (o_dtype != USP_BF16 && o_dtype != USP_FP32) return USP_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return USP_ERR_UNSUPPORTED;
+  if (s_q < 1 || hq < 1 || (double)s_q * hq * d >= 2147483648.0) return USP_ERR_INVALID;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o || !lse) return USP_ERR_NULL;
+  const void* ptrs[] = {o_a, lse_a, o_b, lse_b, o, lse};
   for (const void* p : ptrs)
     if (!aligned16(p)) return USP_ERR_INVALID;
-  if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return USP_ERR_INVALID;
-  const size_t es = elem_bytes(dtype);
-  const size_t qb = (size_t)s_pad * hq * d * es, kb = (size_t)s_pad * hkv * d * es;
-  const size_t lb = (size_t)s_pad * hq * sizeof(float);
-  const size_t need = usp_attn_bwd_workspace_bytes(s_pad, hq, hkv, d, dtype);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return USP_ERR_WORKSPACE;
-  if (need > 0 && !aligned16(workspace)) return USP_ERR_INVALID;
-  const Span ins[] = {{q, qb}, {k, kb}, {v, kb}, {o, qb}, {lse, lb}, {dout, qb}};
-  const Span outs[] = {{dq, qb}, {dk, kb}, {dv, kb}, {workspace, need}};
-  for (const Span& a : outs)
-    for (const Span& b : ins)
-      if (overlap(a, b)) return USP_ERR_INVALID;
-  for (int i = 0; i < 4; ++i)
-    for (int j = i + 1; j < 4; ++j)
-      if (overlap(outs[i], outs[j])) return USP_ERR_INVALID;
-  usp::AttnArgs a{};
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.workspace = workspace;
-  a.s_pad = s_pad; a.s_valid = s_valid; a.cu = cu_seqlens; a.n_docs = n_docs;
-  a.hq = hq; a.hkv = hkv; a.d = d; a.scale = softmax_scale; a.causal = causal;
-  a.stream = static_cast<hipStream_t>(stream);
-  return dtype == USP_BF16 ? usp::attn_bwd_bf16(a) : usp::attn_bwd_f32(a);
+  const size_t ob = (size_t)s_q * hq * d * 4, lb = (size_t)s_q * hq * 4;
+  const size_t oob = (size_t)s_q * hq * d * elem_bytes(o_dtype);
+  // the outputs may BE an input (in-place accumulation), never partly overlap one
+  const Span o_ins[] = {{o_a, ob}, {o_b, ob}, {lse_a, lb}, {lse_b, lb}};
+  for (const Span& b : o_ins) {
+    const bool same = b.p == o && b.n == oob && (b.p == o_a || b.p == o_b);
+    if (!same && overlap({o, oob}, b)) return USP_ERR_INVALID;
+  }
+  for (const Span& b : o_ins) {
+    const bool same = b.p == lse && (b.p == lse_a || b.p == lse_b);
+    if (!same && overlap({lse, lb}, b)) return USP_ERR_INVALID;
+  }
+  if (overlap({o, oob}, {lse, lb})) return USP_ERR_INVALID;
+  return usp::attn_merge_launch(o_a, lse_a, o_b, lse_b, o, lse, s_q, hq, d,
+                                o_dtype == USP_FP32, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "usp_internal.h"
+
 namespace usp {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -70,22 +72,46 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 }
 
 // Document bounds of position i from packed-sequence offsets cu[0..n_docs]
-// (binary search; every index stays in [0, n_docs]). Without cu the whole
-// padded sequence is one document.
+// (binary search; every index stays in [0, n_docs]; bounds clamped to
+// [0, lim]). Without cu every position belongs to one document [0, lim).
 struct DocBounds {
   int lo, hi;  // [lo, hi)
 };
-__device__ __forceinline__ DocBounds doc_bounds(const int32_t* cu, int n_docs, int i, int s_pad) {
-  if (cu == nullptr) return {0, s_pad};
+__device__ __forceinline__ DocBounds doc_bounds(const int32_t* cu, int n_docs, int i, int lim) {
+  if (cu == nullptr) return {0, lim};
   int a = 0, b = n_docs - 1;  // find largest k in [0, n_docs-1] with cu[k] <= i
   while (a < b) {
     int m = (a + b + 1) >> 1;
     if (cu[m] <= i) a = m; else b = m - 1;
   }
   int lo = cu[a], hi = cu[a + 1];
-  lo = lo < 0 ? 0 : (lo > s_pad ? s_pad : lo);
-  hi = hi < lo ? lo : (hi > s_pad ? s_pad : hi);
+  lo = lo < 0 ? 0 : (lo > lim ? lim : lo);
+  hi = hi < lo ? lo : (hi > lim ? lim : hi);
   return {lo, hi};
+}
+
+// Allowed keys of local row r: the contiguous range [lo, hi] of local key
+// indices (hi < lo when empty). Both ends are nondecreasing in r.
+struct KeyRange {
+  int lo, hi;
+};
+__device__ __forceinline__ KeyRange row_keys(const MaskGeom& m, int r) {
+  const int gi = m.q_off + r;
+  const DocBounds b = doc_bounds(m.cu, m.n_docs, gi, m.lim);
+  const int lo = max(b.lo - m.k_off, 0);
+  const int hi = m.causal ? min(gi - m.k_off, m.s_kv - 1) : min(b.hi - m.k_off, m.s_kv) - 1;
+  return {lo, hi};
+}
+
+// Local query rows [lo, hi) that may see local key c (ignoring c < s_kv);
+// lo may be negative, hi <= s_q. Both ends are nondecreasing in c.
+struct RowSpan {
+  int lo, hi;
+};
+__device__ __forceinline__ RowSpan key_rows(const MaskGeom& m, int c) {
+  const int gj = m.k_off + c;
+  const DocBounds b = doc_bounds(m.cu, m.n_docs, gj, m.lim);
+  return {max(b.lo, m.causal ? gj : 0) - m.q_off, min(b.hi - m.q_off, m.s_q)};
 }
 
 // Key-major workspace row length: padded so every 64-key tile is in bounds.

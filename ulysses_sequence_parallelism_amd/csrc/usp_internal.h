@@ -46,6 +46,10 @@ struct FastDiv {
 int permute_launch(bool pack, const void* src, void* dst, int64_t s_real, int64_t s_pad, int p,
                    int64_t row_bytes, hipStream_t stream);
 
+// One attention call. Query rows sit at global positions q_off + [0, s_q),
+// keys at k_off + [0, s_k), of which the first s_kv are valid; lim is the
+// global extent (documents are clamped to it). The full-sequence entry points
+// use q_off = k_off = 0, s_q = s_k = lim = s_pad and s_kv = s_valid.
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -59,24 +63,55 @@ struct AttnArgs {
   void* dk;
   void* dv;
   void* workspace;
-  int64_t s_pad, s_valid;
+  int64_t s_q, s_k, s_kv, q_off, k_off, lim;
   const int32_t* cu;
   int n_docs;
   int hq, hkv, d;
   float scale;
   int causal;
+  int out_f32;     // outputs (O, or dQ/dK/dV) are fp32 instead of bf16
+  int accumulate;  // backward, fp32 outputs: add to the existing contents
   hipStream_t stream;
 };
+
+// Mask geometry on global positions, as the kernels see it. Query row r of a
+// call sits at global position q_off + r, key c at k_off + c; key c is allowed
+// for row r iff c < s_kv, both positions lie in one document and, when causal,
+// the key's position does not exceed the row's.
+struct MaskGeom {
+  const int32_t* cu;
+  int n_docs, lim;     // documents, position clamp (global extent)
+  int q_off, k_off;    // global position of local row 0 / key 0
+  int s_q, s_k, s_kv;  // query rows, key rows, valid key rows
+  int causal;
+};
+
+inline MaskGeom mask_geom(const AttnArgs& a) {
+  MaskGeom m{};
+  m.cu = a.cu;
+  m.n_docs = a.n_docs;
+  m.lim = (int)a.lim;
+  m.q_off = (int)a.q_off;
+  m.k_off = (int)a.k_off;
+  m.s_q = (int)a.s_q;
+  m.s_k = (int)a.s_k;
+  m.s_kv = (int)a.s_kv;
+  m.causal = a.causal;
+  return m;
+}
 
 int kmajor_launch(const void* src, void* dst, int64_t s_pad, int heads, int64_t s_t,
                   hipStream_t stream, const char* trace_name);
 
-size_t attn_fwd_bf16_workspace(int64_t s_pad, int hq, int hkv, int d);
-size_t attn_bwd_bf16_workspace(int64_t s_pad, int hq, int hkv, int d);
+size_t attn_fwd_bf16_workspace(int64_t s_k, int hq, int hkv, int d);
+size_t attn_bwd_bf16_workspace(int64_t s_q, int64_t s_k, int hq, int hkv, int d);
 int attn_fwd_bf16(const AttnArgs& a);
 int attn_bwd_bf16(const AttnArgs& a);
 int attn_fwd_f32(const AttnArgs& a);
 int attn_bwd_f32(const AttnArgs& a);
-size_t attn_bwd_f32_workspace(int64_t s_pad, int hq, int hkv, int d);
+size_t attn_bwd_f32_workspace(int64_t s_q, int hq, int hkv, int d);
+int attn_merge_launch(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
+                      void* o, float* lse, int64_t s_q, int hq, int d, int out_f32,
+                      hipStream_t stream);
 
 }  // namespace usp
