@@ -14,6 +14,17 @@ line also carries forward-only and forward+backward attention rates, the
 permute bandwidth of the composite pack (all P ranks' Q, K and V), the
 roofline of the dominant kernel (live HIP-event timing through the library's
 kernel trace) and the CPU oracle timed on a bounded sample.
+
+--path selects other layouts of the same attention (one JSON line each, no
+pack/unpack, no CPU baseline):
+  ring   one GPU's share of USP with Ulysses degree U = P / R and ring degree
+         R on the same P GPUs: the heads of one Ulysses group (H/U query,
+         H_kv/U key/value heads) and the LAST ring rank's block of S/R query
+         rows against all R key blocks in ring order (its own block first),
+         fp32 partials merged in place, the backward accumulated in fp32
+  cp     the heaviest rank of a C-way contiguous context-parallel split: its
+         query rows (global offset) against every key up to its last row
+  bidir  bidirectional (non-causal) attention over the whole share
 """
 from __future__ import annotations
 
@@ -41,6 +52,9 @@ def parse():
     ap.add_argument("--workload", default="s120k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=24000)
+    ap.add_argument("--path", choices=("ulysses", "ring", "cp", "bidir"), default="ulysses")
+    ap.add_argument("--ring", type=int, default=4, help="ring degree R for --path ring")
+    ap.add_argument("--cp", type=int, default=8, help="context-parallel degree for --path cp")
     ap.add_argument("--counters", action="store_true",
                     help="for rocprofv3 --pmc runs: one warm-up step, one step, then a plain "
                          "1 GiB device copy that calibrates the byte counters; no JSON line")
@@ -127,6 +141,172 @@ def cpu_baseline(w, rows: int):
             "seconds": dt, "cpu": platform.processor() or platform.machine()}
 
 
+def rows_pairs(a: int, b: int, s_valid: int) -> int:
+    """Allowed (row, key) pairs of causal rows [a, b) with keys < s_valid."""
+    c = min(max(s_valid, a), b)  # rows [a, c) see i + 1 keys, rows [c, b) see s_valid
+    return causal_pairs(c) - causal_pairs(a) + (b - c) * s_valid
+
+
+def interval_path(args, w, dev, share, full):
+    """Timed fwd+bwd of the ring, cp or bidir layout; prints one JSON line."""
+    import torch
+
+    import ulysses_sequence_parallelism_amd as usp
+    import workloads
+
+    q, k, v, do = (share[t] for t in (workloads.Q, workloads.K, workloads.V, workloads.DO))
+    s_pad, hq, hkv, d = q.shape[0], w.hq, w.hkv, w.d
+    f32 = dict(dtype=torch.float32, device=dev)
+    if args.path == "ring":
+        r = args.ring
+        if r < 1 or w.p % r or w.hkv_full % (w.p // r) or s_pad % r:
+            print(f"--ring {r}: needs R | P={w.p}, (P/R) | H_kv and R | s_pad", file=sys.stderr)
+            sys.exit(2)
+        u = w.p // r
+        hq, hkv = w.hq_full // u, w.hkv_full // u
+        group = {}
+        for t, x in full.items():  # Ulysses head group 0, every row, zero padding rows
+            y = torch.zeros((s_pad, x.shape[1] // u, d), dtype=x.dtype, device=dev)
+            y[: w.s] = x[:, : x.shape[1] // u]
+            group[t] = y
+        q, k, v, do = (group[t] for t in (workloads.Q, workloads.K, workloads.V, workloads.DO))
+    full.clear()
+    torch.cuda.synchronize()
+    ws_f = torch.empty(usp.usp_attn_fwd_workspace_bytes(s_pad, hq, hkv, d, 0), dtype=torch.uint8,
+                       device=dev)
+    ws_b = torch.empty(usp.usp_attn_bwd_workspace_bytes(s_pad, hq, hkv, d, 0), dtype=torch.uint8,
+                       device=dev)
+    if args.path == "ring":
+        blk = s_pad // r
+        qa, qb = (r - 1) * blk, s_pad                      # the last ring rank's query rows
+        order = [r - 1] + list(range(r - 2, -1, -1))      # own block, then the ring's others
+        pairs_alg = rows_pairs(qa, qb, w.s)
+        qs, dos = q[qa:qb], do[qa:qb]
+        o_fin = torch.empty_like(qs)
+        acc_o, acc_l = torch.empty((blk, hq, d), **f32), torch.empty((hq, blk), **f32)
+        part_o, part_l = torch.empty((blk, hq, d), **f32), torch.empty((hq, blk), **f32)
+        dq = torch.empty((blk, hq, d), **f32)
+        dk = torch.empty((s_pad, hkv, d), **f32)
+        dv = torch.empty((s_pad, hkv, d), **f32)
+
+        def fwd():
+            for step_i, j in enumerate(order):
+                ka, kb = j * blk, (j + 1) * blk
+                skv = max(0, min(kb, w.s) - ka)
+                last = step_i == r - 1
+                o_out, l_out = (acc_o, acc_l) if step_i == 0 else (part_o, part_l)
+                if r == 1:
+                    o_out = o_fin
+                usp.usp_attn_fwd_interval(qs, k[ka:kb], v[ka:kb], q_off=qa, k_off=ka,
+                                          s_k_valid=skv, softmax_scale=w.scale, out=o_out,
+                                          lse=l_out, workspace=ws_f)
+                if step_i > 0:
+                    usp.usp_attn_merge(acc_o, acc_l, part_o, part_l,
+                                       out=o_fin if last else acc_o, lse=acc_l)
+
+        def bwd():
+            for t in (dq, dk, dv):
+                t.zero_()
+            for j in order:
+                ka, kb = j * blk, (j + 1) * blk
+                skv = max(0, min(kb, w.s) - ka)
+                usp.usp_attn_bwd_interval(qs, k[ka:kb], v[ka:kb], o_fin, acc_l, dos, q_off=qa,
+                                          k_off=ka, s_k_valid=skv, softmax_scale=w.scale,
+                                          accumulate=True, dq=dq, dk=dk[ka:kb], dv=dv[ka:kb],
+                                          workspace=ws_b)
+        desc = (f"{w.name}: USP on {w.p} GPUs as Ulysses {u} x Ring {r}: one GPU's share is "
+                f"{hq} Q / {hkv} KV heads and the last ring rank's query rows [{qa}, {qb}) "
+                f"against all {r} key blocks of {blk} in ring order; fp32 partials + in-place "
+                f"LSE merge, fp32 accumulated backward; S={w.s}, d={d}, causal")
+        causal = True
+    elif args.path == "cp":
+        c = args.cp
+        a, b = s_pad * (c - 1) // c, s_pad
+        pairs_alg = rows_pairs(a, b, w.s)
+        o = torch.empty((b - a, hq, d), dtype=q.dtype, device=dev)
+        lse = torch.empty((hq, b - a), **f32)
+        dq = torch.empty((b - a, hq, d), **f32)
+        dk = torch.empty((b, hkv, d), **f32)
+        dv = torch.empty((b, hkv, d), **f32)
+        qs, dos = q[a:b], do[a:b]
+
+        def fwd():
+            usp.usp_attn_fwd_interval(qs, k[:b], v[:b], q_off=a, k_off=0, softmax_scale=w.scale,
+                                      out=o, lse=lse, workspace=ws_f)
+
+        def bwd():
+            usp.usp_attn_bwd_interval(qs, k[:b], v[:b], o, lse, dos, q_off=a, k_off=0,
+                                      softmax_scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+        desc = (f"{w.name}: last rank of a {c}-way contiguous context-parallel split, query rows "
+                f"[{a}, {b}) against keys [0, {b}), causal with the global offset; bf16 O, fp32 "
+                f"gradients; {hq} Q / {hkv} KV heads, d={d}")
+        causal = True
+    else:
+        pairs_alg = s_pad * w.s
+        o = torch.empty_like(q)
+        lse = torch.empty((hq, s_pad), **f32)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+        def fwd():
+            usp.usp_attn_fwd(q, k, v, s_valid=w.s, causal=False, softmax_scale=w.scale, out=o,
+                             lse=lse, workspace=ws_f)
+
+        def bwd():
+            usp.usp_attn_bwd(q, k, v, o, lse, do, s_valid=w.s, causal=False,
+                             softmax_scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+        desc = (f"{w.name} rank share, bidirectional (no causal mask), keys past {w.s} masked; "
+                f"{hq} Q / {hkv} KV heads, d={d}")
+        causal = False
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    usp.usp_trace_enable(True)
+    usp.usp_trace_collect()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    usp.usp_trace_enable(False)
+    trace = usp.usp_trace_collect()
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+    per = {e["name"]: e for e in trace}
+    f_fwd, f_bwd = 4 * d * hq * pairs_alg, 10 * d * hq * pairs_alg
+    fwd_names = ("attn_fwd_kmajor_v", "attn_fwd_bf16", "attn_merge")
+    fwd_ms = sum(per[n]["total_ms"] for n in fwd_names if n in per) / args.steps
+    bwd_ms = sum(e["total_ms"] for e in trace if e["name"] not in fwd_names) / args.steps
+    # dominant kernel: its algorithmic FLOPs summed over its launches / its summed time
+    dom = max((e for e in trace if e["name"] in KERNELS), key=lambda e: e["total_ms"])
+    dom_flops = KERNELS[dom["name"]][1] * d * hq * pairs_alg
+    achieved = dom_flops / (dom["total_ms"] / args.steps * 1e-3) / 1e12
+    out = {
+        "metric": f"attn TFLOP/s fwd+bwd, {args.path} layout",
+        "value": round((f_fwd + f_bwd) / (step_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": desc, "seq_len": w.s, "heads_q": hq, "heads_kv": hkv,
+                   "head_dim": d, "causal": causal, "path": args.path},
+        "attn_fwd_ms": round(fwd_ms, 3), "attn_bwd_ms": round(bwd_ms, 3),
+        "attn_fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 1),
+        "attn_fwd_bwd_tflops": round((f_fwd + f_bwd) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 1),
+        "kernels_ms_per_step": {e["name"]: round(e["total_ms"] / args.steps, 4) for e in trace},
+        "kernel_launches_per_step": {e["name"]: e["launches"] // args.steps for e in trace},
+        "roofline": {"bound": "mfma", "kernel": dom["name"], "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flop_per_step": dom_flops},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -156,6 +336,9 @@ def main():
         full[t] = workloads.tensor(w, t).to(dev)
     # this rank's share: the composite pack's slice 0 (what the all-to-all delivers)
     share = {t: usp.usp_pad_pack_seq2head(x, p)[0].contiguous() for t, x in full.items()}
+    if args.path != "ulysses":
+        interval_path(args, w, dev, share, full)
+        return
     q, k, v, do = (share[t] for t in (workloads.Q, workloads.K, workloads.V, workloads.DO))
     # this rank's own sequence slice (all heads): what it packs into send buffers
     local = {t: x[:s_loc].contiguous() for t, x in full.items()}

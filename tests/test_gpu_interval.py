@@ -324,3 +324,62 @@ def test_bf16_ring4_on_32k_share_sampled_rows():
     say(f"  ring vs single call: max {diff.max().item():.3e} mean {diff.mean().item():.3e}")
     assert diff.max().item() <= 2e-2 and diff.mean().item() <= 2e-3
     torch.testing.assert_close(acc_l, lse_full, rtol=0, atol=2e-2)
+
+
+def test_bf16_usp_ulysses2_ring4_last_rank_120k():
+    """One GPU's share of USP on 8 GPUs as Ulysses 2 x Ring 4 at S = 120000:
+    the heads of Ulysses group 0 (16 Q / 4 KV), the last ring rank's 30000
+    query rows against the four key blocks in ring order. Merged O / LSE and
+    the accumulated dQ on sampled rows, and dK / dV of the sequence's last
+    keys (seen only by this rank's rows), against the oracle's full-sequence
+    attention."""
+    L = usp()
+    dev = gpu()
+    w = workloads.WORKLOADS["s120k"]
+    u, r = 2, 4
+    hq, hkv = w.hq_full // u, w.hkv_full // u
+    s = w.s
+    say(f"USP U{u}xR{r} at S={s}: {hq} Q / {hkv} KV heads")
+    x = {}
+    for t in (workloads.Q, workloads.K, workloads.V, workloads.DO):
+        full = workloads.tensor(w, t)
+        x[t] = full[:, : full.shape[1] // u].contiguous()
+        del full
+    q, k, v, do = (x[t].to(dev) for t in (workloads.Q, workloads.K, workloads.V, workloads.DO))
+    blk = s // r
+    qa, qb = (r - 1) * blk, s
+    acc_o = acc_l = None
+    for j in [r - 1] + list(range(r - 2, -1, -1)):
+        ka, kb = j * blk, (j + 1) * blk
+        o_p, l_p = L.usp_attn_fwd_interval(q[qa:qb], k[ka:kb], v[ka:kb], q_off=qa, k_off=ka,
+                                           softmax_scale=w.scale)
+        if acc_o is None:
+            acc_o, acc_l = o_p, l_p
+        else:
+            L.usp_attn_merge(acc_o, acc_l, o_p, l_p, out=acc_o, lse=acc_l)
+    o_fin = acc_o.to(torch.bfloat16)
+    dq = torch.zeros((blk, hq, w.d), dtype=torch.float32, device=dev)
+    dk = torch.zeros((s, hkv, w.d), dtype=torch.float32, device=dev)
+    dv = torch.zeros((s, hkv, w.d), dtype=torch.float32, device=dev)
+    for j in range(r):
+        ka, kb = j * blk, (j + 1) * blk
+        L.usp_attn_bwd_interval(q[qa:qb], k[ka:kb], v[ka:kb], o_fin, acc_l, do[qa:qb], q_off=qa,
+                                k_off=ka, softmax_scale=w.scale, accumulate=True, dq=dq,
+                                dk=dk[ka:kb], dv=dv[ka:kb])
+    torch.cuda.synchronize()
+    g = np.random.default_rng([w.cfg, 7, 9])
+    rows = np.unique(np.concatenate([np.arange(qa, qa + 8), np.arange(qb - 8, qb),
+                                     g.integers(qa, qb, size=48)]))
+    q64, k64, v64, do64 = (f64(x[t]) for t in (workloads.Q, workloads.K, workloads.V, workloads.DO))
+    say(f"  oracle on {len(rows)} rows")
+    o_ref, lse_ref = oracle.attn_fwd_rows(q64, k64, v64, rows, w.scale)
+    check_close("USP O[rows]", f64(acc_o)[rows - qa], o_ref, "bf16", bf16_out=False)
+    check_close("USP LSE[rows]", f64(acc_l)[:, rows - qa], lse_ref, "bf16")
+    dq_ref = oracle.attn_bwd_rows(q64, k64, v64, do64, rows, w.scale)
+    check_close("USP dQ[rows]", f64(dq)[rows - qa], dq_ref, "bf16", bf16_out=False)
+    keys = np.arange(s - 24, s)
+    dk_ref, dv_ref = oracle.attn_bwd_keys(q64, k64, v64, do64, keys, w.scale)
+    check_close("USP dK[tail]", f64(dk)[keys], dk_ref, "bf16", bf16_out=False)
+    check_close("USP dV[tail]", f64(dv)[keys], dv_ref, "bf16", bf16_out=False)
+    # keys of the first block are seen by every one of this rank's rows: finite, nonzero
+    assert torch.isfinite(dk).all() and torch.isfinite(dv).all() and dk[:blk].abs().sum() > 0
