@@ -203,16 +203,9 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
       if (it + 2 < nt) load_k(it + 2);
       if (it + 1 < nt) load_v(it + 1);
 
-      // -- row max of this tile; a full tile needs no mask
-      float m4[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x16& a = scur[q >> 1];
-        const int o = (q & 1) * 8;
-        m4[q] = fmaxf(fmaxf(fmaxf(a[o], a[o + 1]), fmaxf(a[o + 2], a[o + 3])),
-                      fmaxf(fmaxf(a[o + 4], a[o + 5]), fmaxf(a[o + 6], a[o + 7])));
-      }
-      float mx = half_swap_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * pr.scale_log2;
+      // -- row max of this tile (both half-waves hold the row); a full tile
+      //    needs no mask
+      float mx = half_swap_max(max_of_32(scur[0], scur[1])) * pr.scale_log2;
       const bool full = t0 >= free_lo && t0 + BN - 1 <= free_hi &&
                         t0 >= wkmin && t0 + BN - 1 <= wkmax;
       // -- slow path (boundary tiles and running-max updates, both rare): mask,
@@ -226,12 +219,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
               const int key = t0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
               if (key < lo || key > hi) scur[kb][i] = -INFINITY;
             }
-          float m = scur[0][0];
-#pragma unroll
-          for (int i = 1; i < 16; ++i) m = fmaxf(m, scur[0][i]);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) m = fmaxf(m, scur[1][i]);
-          mx = half_swap_max(m) * pr.scale_log2;
+          mx = half_swap_max(max_of_32(scur[0], scur[1])) * pr.scale_log2;
         }
         const bool need = mx > m_run + kRescaleThreshold;
         if (__ballot(need)) {
@@ -281,6 +269,23 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
           oacc[b] = mfma32(*reinterpret_cast<const bf16x8*>(vp + ch * 16), pb[ch], oacc[b]);
         }
       }
+#ifdef FWD_SCHED
+      // score MFMAs interleaved with the probability VALU work, then the O
+      // MFMAs with the rest
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, FWD_SCHED, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+      }
+#endif
 
       if (it + 2 < nt) store_k(it & 1);
       if (it + 1 < nt) store_v((it + 1) & 1);

@@ -59,6 +59,25 @@ __device__ __forceinline__ void half_pair(float x, float& lo, float& hi) {
   lo = __builtin_bit_cast(float, a);
   hi = __builtin_bit_cast(float, b);
 }
+// Maximum of the 32 values of two accumulator tiles as a tree of 3-input
+// maxima (16 v_max3_f32, depth 4). The kernels are built without NaN
+// semantics (no NaN can arise: masked scores are -inf and every -inf - -inf
+// is guarded), so no canonicalising instructions are inserted.
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+__device__ __forceinline__ float max_of_32(const f32x16& x, const f32x16& y) {
+  float l1[12];
+#pragma unroll
+  for (int g = 0; g < 5; ++g) l1[g] = max3f(x[3 * g], x[3 * g + 1], x[3 * g + 2]);
+  l1[5] = max3f(x[15], y[0], y[1]);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) l1[6 + g] = max3f(y[2 + 3 * g], y[3 + 3 * g], y[4 + 3 * g]);
+  l1[10] = y[14];
+  l1[11] = y[15];
+  const float a = max3f(l1[0], l1[1], l1[2]), b = max3f(l1[3], l1[4], l1[5]);
+  const float c = max3f(l1[6], l1[7], l1[8]), e = max3f(l1[9], l1[10], l1[11]);
+  return fmaxf(max3f(a, b, c), e);
+}
+
 // Combine a value across the two 32-lane halves of a wave64.
 __device__ __forceinline__ float half_swap_max(float x) {
   float lo, hi;
