@@ -55,7 +55,9 @@ constexpr int KP = D + 8;    // row-major tile pitch (elements)
 // D_i = sum_d dO[i][h][d] * O[i][h][d]  (fp32 from the bf16 values)
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const __bf16* __restrict__ o,
                                                          const __bf16* __restrict__ dout,
-                                                         float* __restrict__ dd, int s_q,
+                                                         const float* __restrict__ lse,
+                                                         float* __restrict__ dd,
+                                                         float* __restrict__ lse2, int s_q,
                                                          int hq, int64_t s_t) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 16 lanes per (row, head)
   const int64_t rh = t >> 4;
@@ -76,6 +78,7 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const __bf16* __restric
   if (live && part == 0) {
     const int i = (int)(rh / hq), h = (int)(rh % hq);
     dd[(int64_t)h * s_t + i] = s;
+    lse2[(int64_t)h * s_t + i] = lse[(int64_t)h * s_q + i] * kLog2e;
   }
 }
 
@@ -88,6 +91,7 @@ struct BwdParams {
   const __bf16* dot;   // key-major dO  [hq][D][s_tq]
   const __bf16* kt;    // key-major K   [hkv][D][s_tk]
   const float* lse;    // [hq][s_q]
+  const float* lse2;   // LSE * log2(e), [hq][s_tq]
   const float* dd;     // [hq][s_tq]
   void* dq;            // [s_q][hq][D]
   void* dk;            // [s_k][hkv][D]
@@ -140,19 +144,32 @@ __device__ __forceinline__ void store_rows(void* out, int64_t off, const f32x16 
 // halves each wave's live state (one stationary operand, one accumulator), so
 // two waves fit per SIMD and one wave's MFMAs overlap the other's softmax and
 // LDS traffic.
+//
+// Tiles go from global memory straight into LDS (global_load_lds_dwordx4: no
+// staging registers, no LDS stores). That load writes each lane's 16 bytes at
+// consecutive LDS addresses, so rows cannot be padded; instead the 16-byte
+// chunks of a row are XOR-swizzled: chunk c of a 256-byte Q / dO row r sits in
+// slot c ^ (r & 15), chunk c of a 128-byte Q^T / dO^T row r in slot
+// c ^ ((r >> 1) & 7). Each lane fetches the chunk its slot holds, and the
+// fragment reads (32 rows, one chunk) hit 16 distinct bank groups per 16 lanes.
 template <int BQ>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
+  static_assert(BQ == 64, "the direct-load tile mapping assumes 64-row tiles");
   constexpr int MB = BQ / 32;          // 32-row blocks per tile
   constexpr int NCH = 2 * MB;          // 16-row chunks per tile
-  constexpr int TQ = BQ + 8;           // key-major tile pitch (elements)
-  constexpr int RCH = BQ / 32;         // 16-byte chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) __bf16 lq[2][BQ * KP];
-  __shared__ __attribute__((aligned(16))) __bf16 ldo[2][BQ * KP];
-  __shared__ __attribute__((aligned(16))) __bf16 lqt[2][D * TQ];
-  __shared__ __attribute__((aligned(16))) __bf16 ldot[2][D * TQ];
+  __shared__ __attribute__((aligned(16))) __bf16 lq[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 ldo[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 lqt[2][D * BQ];
+  __shared__ __attribute__((aligned(16))) __bf16 ldot[2][D * BQ];
   __shared__ __attribute__((aligned(16))) float llse[2][BQ];
   __shared__ __attribute__((aligned(16))) float ldd[2][BQ];
   __shared__ __attribute__((aligned(16))) u32x4 lp[4][NCH][64];
+  // These arrays are filled only by direct global->LDS loads, which this
+  // compiler does not count as stores to them: without the escape below it
+  // treats every read of them as undefined and deletes the dependent work.
+  asm volatile("" ::"s"(&lq[0][0]), "s"(&ldo[0][0]), "s"(&lqt[0][0]), "s"(&ldot[0][0]),
+               "s"(&llse[0][0]), "s"(&ldd[0][0])
+               : "memory");
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = w & 3, role = w >> 2;
@@ -202,59 +219,74 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
   const int ntr = (j0 < s_kv && rend >= rstart) ? (rend - tstart) / BQ + 1 : 0;
   const int nt = ntr * g;
 
-  u32x4 sq[RCH], sdo[RCH], sqt[RCH], sdot[RCH];
-  float sld = 0.f;
   // Tile order: query tiles from the END of the sequence downwards, the heads
   // of the group innermost. Every resident workgroup then reads the same
   // (row tile, head) at about the same time, whatever its key block, so the
   // tiles are shared through L2 instead of each workgroup streaming its own
   // row range.
   auto tile_row = [&](int it) { return tstart + (ntr - 1 - it / g) * BQ; };
-  auto load_tile = [&](int it) {
+  // One tile = Q, dO (64 rows x 256 B), Q^T, dO^T (128 rows x 128 B), i.e. 64
+  // wave-loads of 1 KiB, plus the 64 LSE and D values. Rows past the end read
+  // the last row: every load is unconditional and such rows are always masked.
+  // Only the role-0 waves load (role 1 is on the critical path of every tile):
+  // wave 0 loads Q, 1 dO, 2 Q^T, 3 dO^T (16 KiB each), waves 0 and 1 also the
+  // LSE and D of the tile's rows. The address of each load is a wave-uniform
+  // base plus a lane offset; the swizzle makes the lane offsets repeat every 4
+  // parts (row tiles) or 2 parts (transposed tiles), so they are computed once.
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // LDS destinations go to M0
+  int loff[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (wu < 2) {  // row tiles: part = 4 p + k covers rows 16 p + 4 k + lane / 16
+      const int rr = 4 * k + (lane >> 4), c = (lane & 15) ^ rr;
+      loff[k] = ((lane >> 4) * pr.hq) * D + c * 8;
+    } else {       // transposed tiles: part = 2 p + k covers d-rows 16 p + 8 k + lane / 8
+      const int rr = 8 * (k & 1) + (lane >> 3), c = (lane & 7) ^ ((rr >> 1) & 7);
+      loff[k] = (lane >> 3) * (int)pr.s_tq + c * 8;
+    }
+  }
+  auto load_tile = [&](int it, int buf) {
+    if (wu >= 4) return;
     const int h = kvh * g + it % g;
     const int r0 = tile_row(it);
+    if (wu < 2) {
+      const __bf16* base = wu == 0 ? pr.q : pr.dout;
+      __bf16* dst = wu == 0 ? &lq[buf][0] : &ldo[buf][0];
+      if (r0 + BQ <= s_q) {
 #pragma unroll
-    for (int u = 0; u < RCH; ++u) {
-      const int e = tid + 512 * u;
-      const int r = e >> 4, c = e & 15;
-      // rows past the end read the last row instead: every load is
-      // unconditional (no wait is forced before the tile is consumed) and
-      // such rows are always masked
-      const int i = min(r0 + r, s_q - 1);
-      const int64_t off = ((int64_t)i * pr.hq + h) * D + c * 8;
-      sq[u] = *reinterpret_cast<const u32x4*>(pr.q + off);
-      sdo[u] = *reinterpret_cast<const u32x4*>(pr.dout + off);
-      const int dr = e / (BQ / 8), c8 = e % (BQ / 8);
-      const int64_t toff = ((int64_t)h * D + dr) * pr.s_tq + r0 + c8 * 8;
-      sqt[u] = *reinterpret_cast<const u32x4*>(pr.qt + toff);
-      sdot[u] = *reinterpret_cast<const u32x4*>(pr.dot + toff);
-    }
-    {
-      // threads [0, BQ) fetch LSE, [BQ, 2 BQ) fetch D, the rest a dummy
-      const int i = min(r0 + (tid % BQ), s_q - 1);
-      const float* src = tid < BQ ? pr.lse + (int64_t)h * s_q : pr.dd + (int64_t)h * pr.s_tq;
-      sld = src[i];
+        for (int part = 0; part < 16; ++part) {
+          const __bf16* b = base + ((int64_t)(r0 + 4 * part) * pr.hq + h) * D;
+          __builtin_amdgcn_global_load_lds(b + loff[part & 3], dst + part * 512, 16, 0, 0);
+        }
+      } else {  // the last tile: rows past the end read the last row (always masked)
+#pragma unroll
+        for (int part = 0; part < 16; ++part) {
+          const int r = 4 * part + (lane >> 4), c = (lane & 15) ^ (r & 15);
+          const int row = min(r0 + r, s_q - 1);
+          __builtin_amdgcn_global_load_lds(base + ((int64_t)row * pr.hq + h) * D + c * 8,
+                                           dst + part * 512, 16, 0, 0);
+        }
+      }
+      const int i = min(r0 + lane, s_q - 1);
+      const float* src = (wu == 0 ? pr.lse2 : pr.dd) + (int64_t)h * pr.s_tq + i;
+      __builtin_amdgcn_global_load_lds(src, wu == 0 ? &llse[buf][0] : &ldd[buf][0], 4, 0, 0);
+    } else {
+      const __bf16* base = (wu == 2 ? pr.qt : pr.dot) + (int64_t)h * D * pr.s_tq + r0;
+      __bf16* dst = wu == 2 ? &lqt[buf][0] : &ldot[buf][0];
+#pragma unroll
+      for (int part = 0; part < 16; ++part)
+        __builtin_amdgcn_global_load_lds(base + (int64_t)(8 * part) * pr.s_tq + loff[part & 1],
+                                         dst + part * 512, 16, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
+  // per-lane LDS element offsets of the fragment reads (swizzled chunks)
+  int roff[8], toff[NCH];
 #pragma unroll
-    for (int u = 0; u < RCH; ++u) {
-      const int e = tid + 512 * u;
-      const int r = e >> 4, c = e & 15;
-      *reinterpret_cast<u32x4*>(&lq[buf][r * KP + c * 8]) = sq[u];
-      *reinterpret_cast<u32x4*>(&ldo[buf][r * KP + c * 8]) = sdo[u];
-      const int dr = e / (BQ / 8), c8 = e % (BQ / 8);
-      *reinterpret_cast<u32x4*>(&lqt[buf][dr * TQ + c8 * 8]) = sqt[u];
-      *reinterpret_cast<u32x4*>(&ldot[buf][dr * TQ + c8 * 8]) = sdot[u];
-    }
-    if (tid < BQ) llse[buf][tid] = sld * kLog2e;
-    else if (tid < 2 * BQ) ldd[buf][tid - BQ] = sld;
-  };
+  for (int kk = 0; kk < 8; ++kk) roff[kk] = ln * D + (((hl + 2 * kk) ^ (ln & 15)) << 3);
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) toff[ch] = ln * BQ + (((hl + 2 * ch) ^ ((ln >> 1) & 7)) << 3);
 
-  if (nt > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  if (nt > 0) load_tile(0, 0);
   __syncthreads();
 
   for (int it = 0; it < nt; ++it) {
@@ -271,10 +303,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
       for (int mb = 0; mb < MB; ++mb) {
         // all 8 A fragments of the block are requested before its MFMA chain,
         // so the chain waits for one LDS round trip, not one per MFMA pair
-        const __bf16* ap = base + (mb * 32 + ln) * KP + hl * 8;
+        const __bf16* ap = base + mb * 32 * D;
         bf16x8 af[8];
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) af[kk] = *reinterpret_cast<const bf16x8*>(ap + kk * 16);
+        for (int kk = 0; kk < 8; ++kk) af[kk] = *reinterpret_cast<const bf16x8*>(ap + roff[kk]);
         __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the chain
         pa[mb] = f32x16{};
 #pragma unroll
@@ -320,9 +352,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
       }
     }
     __syncthreads();  // P is visible to role 1
-    // next tile's global loads: issued here so their registers are not live
-    // during phase 1; phase 2 covers their latency
-    if (it + 1 < nt) load_tile(it + 1);
+    // next tile straight into the other LDS slot (its last reads were in the
+    // previous tile); phase 2 covers the latency
+    if (it + 1 < nt) load_tile(it + 1, buf ^ 1);
 
     // phase 2: role 0 -> dV^T += dO^T P; role 1 -> dS, dK^T += Q^T dS
     if (active) {
@@ -355,9 +387,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
         bf16x8 af[2][NCH];
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) {
-          const __bf16* tp = tbase + ((b2 + bb) * 32 + ln) * TQ + hl * 8;
+          const __bf16* tp = tbase + (b2 + bb) * 32 * BQ;
 #pragma unroll
-          for (int ch = 0; ch < NCH; ++ch) af[bb][ch] = *reinterpret_cast<const bf16x8*>(tp + ch * 16);
+          for (int ch = 0; ch < NCH; ++ch) af[bb][ch] = *reinterpret_cast<const bf16x8*>(tp + toff[ch]);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the chain
 #pragma unroll
@@ -366,8 +398,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
           for (int bb = 0; bb < 2; ++bb) acc[b2 + bb] = mfma32(af[bb][ch], pb[ch], acc[b2 + bb]);
       }
     }
-    if (it + 1 < nt) store_tile(buf ^ 1);
-    __syncthreads();
+    __syncthreads();  // also waits for the next tile's loads
   }
 
   if (key < s_k)
@@ -568,7 +599,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 size_t attn_bwd_bf16_workspace(int64_t s_q, int64_t s_k, int hq, int hkv, int d) {
   const size_t s_tq = (size_t)kmajor_len(s_q), s_tk = (size_t)kmajor_len(s_k);
   return align256((size_t)hq * d * s_tq * 2) * 2 + align256((size_t)hkv * d * s_tk * 2) +
-         align256((size_t)hq * s_tq * 4);
+         align256((size_t)hq * s_tq * 4) * 2;
 }
 
 int attn_bwd_bf16(const AttnArgs& a) {
@@ -580,6 +611,7 @@ int attn_bwd_bf16(const AttnArgs& a) {
   __bf16* dot = reinterpret_cast<__bf16*>(ws + qt_bytes);
   __bf16* kt = reinterpret_cast<__bf16*>(ws + 2 * qt_bytes);
   float* dd = reinterpret_cast<float*>(ws + 2 * qt_bytes + kt_bytes);
+  float* lse2 = reinterpret_cast<float*>(ws + 2 * qt_bytes + kt_bytes + align256((size_t)a.hq * s_tq * 4));
 
   int rc = kmajor_launch(a.q, qt, a.s_q, a.hq, s_tq, a.stream, "attn_bwd_kmajor");
   if (rc == USP_OK) rc = kmajor_launch(a.dout, dot, a.s_q, a.hq, s_tq, a.stream, "attn_bwd_kmajor");
@@ -589,8 +621,8 @@ int attn_bwd_bf16(const AttnArgs& a) {
     const int64_t n = a.s_q * a.hq * 16;
     TraceScope ts("attn_bwd_rowdot_bf16", a.stream);
     hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, a.stream,
-                       static_cast<const __bf16*>(a.o), static_cast<const __bf16*>(a.dout), dd,
-                       (int)a.s_q, a.hq, s_tq);
+                       static_cast<const __bf16*>(a.o), static_cast<const __bf16*>(a.dout), a.lse,
+                       dd, lse2, (int)a.s_q, a.hq, s_tq);
     if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
   }
   BwdParams p{};
@@ -602,6 +634,7 @@ int attn_bwd_bf16(const AttnArgs& a) {
   p.dot = dot;
   p.kt = kt;
   p.lse = a.lse;
+  p.lse2 = lse2;
   p.dd = dd;
   p.dq = a.dq;
   p.dk = a.dk;

@@ -269,23 +269,6 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
           oacc[b] = mfma32(*reinterpret_cast<const bf16x8*>(vp + ch * 16), pb[ch], oacc[b]);
         }
       }
-#ifdef FWD_SCHED
-      // score MFMAs interleaved with the probability VALU work, then the O
-      // MFMAs with the rest
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, FWD_SCHED, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
-      }
-#endif
 
       if (it + 2 < nt) store_k(it & 1);
       if (it + 1 < nt) store_v((it + 1) & 1);
