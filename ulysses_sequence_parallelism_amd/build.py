@@ -72,6 +72,15 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    # a kernel whose host launch stub was not emitted shows up only as an
+    # undefined symbol of the library's own namespace: fail the build on it
+    nm = shutil.which("nm")
+    if nm:
+        und = subprocess.run([nm, "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
+        own = [ln.split()[-1] for ln in und.splitlines() if "_ZN3usp" in ln]
+        if own:
+            os.remove(tmp)
+            raise RuntimeError("libusp.so has undefined internal symbols: " + ", ".join(own))
     os.replace(tmp, LIB)
     return LIB
 
