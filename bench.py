@@ -304,6 +304,18 @@ def interval_path(args, w, dev, share, full):
                      "algorithmic_flop_per_step": dom_flops},
         "cpu_baseline": None,
     }
+    if args.path == "ring" and "attn_merge" in per:
+        # the merge is HBM-bound: per (row, head) it reads two fp32 O rows and
+        # two LSEs and writes one O row (fp32 for the first r-2 merges, bf16
+        # for the last) and one LSE
+        blk = s_pad // args.ring
+        rh = blk * hq
+        nbytes = (r - 2) * rh * (d * 12 + 12) + rh * (d * 10 + 12)
+        mms = per["attn_merge"]["total_ms"] / args.steps
+        out["merge"] = {"launches_per_step": per["attn_merge"]["launches"] // args.steps,
+                        "bytes_per_step": nbytes, "ms_per_step": round(mms, 4),
+                        "gbps": round(nbytes / (mms * 1e-3) / 1e9, 1),
+                        "frac_of_hbm_peak": round(nbytes / (mms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     print(json.dumps(out), flush=True)
 
 
