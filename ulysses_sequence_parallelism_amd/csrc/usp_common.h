@@ -37,6 +37,39 @@ __host__ __device__ __forceinline__ int kperm(int p) {
   return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
 }
 
+// Slot of 16-byte chunk c in a 256-byte LDS row r (16 chunks): c ^ swz16(r).
+// swz16 rotates the low four row bits by two, so both access patterns of the
+// attention tiles touch 16 distinct slots: one chunk of 16 consecutive rows
+// (row-major fragment reads) and 4 consecutive chunks of 4 consecutive rows
+// starting at a multiple of 4 (transposed reads).
+__host__ __device__ __forceinline__ int swz16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Transposed LDS read (ds_read_b64_tr_b16). Lanes act in groups of 16: each
+// names 4 consecutive bf16 values, and lane i of a group receives value i%4
+// of the values named by lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4 of its
+// group, in that order.
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_v;
+__device__ __forceinline__ bf16x4_v lds_read_tr(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) bf16x4_v*)(const_cast<__bf16*>(p)));
+}
+
+// Element offset, in a tile of 128-element rows stored with swz16, that lane
+// `lane` names in transposed read h (0 or 1) of column block b, for the
+// 16-row chunk at row 0. Reads h = 0 and h = 1 together give the lane column
+// 32b + lane%32 of rows 8h + 4(lane/32) + j, j = 0..3: the 32x32x16 operand
+// (m = column, k = row) in the k-order in which the other operand leaves a
+// 32x32 accumulator (see kperm).
+__device__ __forceinline__ int tr_offset(int lane, int b, int h) {
+  const int r = 8 * h + 4 * (lane >> 5) + ((lane >> 2) & 3);
+  const int c = 4 * b + 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
+  return r * 128 + ((c ^ swz16(r)) << 3) + 4 * (lane & 1);
+}
+__device__ __forceinline__ bf16x8 frag_tr(const __bf16* tile, int off0, int off1) {
+  const bf16x4_v a = lds_read_tr(tile + off0), b = lds_read_tr(tile + off1);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
   f32x2 v = {a, b};
   bf16x2 r = __builtin_convertvector(v, bf16x2);  // v_cvt_pk_bf16_f32, RNE
