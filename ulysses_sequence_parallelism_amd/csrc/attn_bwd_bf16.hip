@@ -44,6 +44,9 @@
 #ifndef DKDV_ROWS
 #define DKDV_ROWS 64
 #endif
+#ifndef DKDV_GROUPS
+#define DKDV_GROUPS 4
+#endif
 
 namespace usp {
 
@@ -131,9 +134,11 @@ __device__ __forceinline__ void store_rows(void* out, int64_t off, const f32x16 
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV: key-stationary. A workgroup owns 128 keys of one KV head (four
-// groups of 32) and walks every query tile (BQ rows) of every query head of
-// the group that can see them. Each key group is served by a PAIR of waves:
+// dK / dV: key-stationary. A workgroup owns KG groups of 32 keys of one KV
+// head (KG = 4: 128 keys, 8 waves, one workgroup per CU; KG = 2 runs two
+// 4-wave workgroups per CU and measured 10% slower at 120K) and walks every
+// query tile (BQ rows) of every query head of the group that can see them.
+// Each key group is served by a PAIR of waves:
 //   role 0: S = Q K^T -> P -> dV^T += dO^T P   (K fragments stationary)
 //   role 1: dP = dO V^T -> dS = P (dP - D) -> dK^T += Q^T dS   (V stationary)
 // P crosses from role 0 to role 1 through LDS in accumulator register order
@@ -150,8 +155,10 @@ __device__ __forceinline__ void store_rows(void* out, int64_t off, const f32x16 
 // phase-2 operands (Q^T, dO^T with rows = d) are read from the same tiles with
 // transposed LDS reads, in the row order in which P and dS leave the
 // accumulators. Both read patterns are conflict-free under swz16.
-template <int BQ>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
+template <int BQ, int KG>
+__global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(BwdParams pr) {
+  static_assert(KG == 2 || KG == 4, "2 or 4 key groups per workgroup");
+  constexpr int KEYS = 32 * KG;        // keys per workgroup
   static_assert(BQ == 64, "the direct-load tile mapping assumes 64-row tiles");
   constexpr int MB = BQ / 32;          // 32-row blocks per tile
   constexpr int NCH = 2 * MB;          // 16-row chunks per tile
@@ -159,7 +166,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
   __shared__ __attribute__((aligned(16))) __bf16 ldo[2][BQ * D];
   __shared__ __attribute__((aligned(16))) float llse[2][BQ];
   __shared__ __attribute__((aligned(16))) float ldd[2][BQ];
-  __shared__ __attribute__((aligned(16))) u32x4 lp[4][NCH][64];
+  __shared__ __attribute__((aligned(16))) u32x4 lp[KG][NCH][64];
   // These arrays are filled only by direct global->LDS loads, which this
   // compiler does not count as stores to them: without the escape below it
   // treats every read of them as undefined and deletes the dependent work.
@@ -167,13 +174,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
                : "memory");
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int grp = w & 3, role = w >> 2;
+  const int grp = w % KG, role = w / KG;
   const int hl = lane >> 5, ln = lane & 31;
   const int s_q = pr.m.s_q, s_k = pr.m.s_k, s_kv = pr.m.s_kv;
   const int g = pr.hq / pr.hkv;
   const int kvh = blockIdx.y;
-  const int j0 = blockIdx.x * 128;
-  const int j1 = min(j0 + 128, s_k);
+  const int j0 = blockIdx.x * KEYS;
+  const int j1 = min(j0 + KEYS, s_k);
   const int wj0 = j0 + grp * 32;
   const int key = wj0 + ln;
   const int kc = min(key, s_k - 1);
@@ -224,32 +231,35 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
   // 64 LSE and D values. Rows past the end read the last row: every load is
   // unconditional and such rows are always masked. The next tile is loaded at
   // the top of each tile by the role-1 waves, whose first phase is the shorter
-  // one: waves 4 and 5 bring Q (parts 0-7 and 8-15, 4 rows each), waves 6 and
-  // 7 dO, waves 4 and 6 also the LSE and D of the tile's rows. The address of
-  // each load is a wave-uniform base plus a lane offset; the swizzle makes the
-  // lane offsets repeat every 4 parts, so they are computed once.
+  // one: the first half of them bring Q, the second half dO (16 parts of 4
+  // rows each, split evenly), and the first wave of each half also the LSE or
+  // D of the tile's rows. The address of each load is a wave-uniform base plus
+  // a lane offset; the swizzle makes the lane offsets repeat every 4 parts, so
+  // they are computed once.
   const int wu = __builtin_amdgcn_readfirstlane(w);  // LDS destinations go to M0
   int loff[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k)  // part = 4 p + k covers rows 16 p + 4 k + lane / 16
     loff[k] = ((lane >> 4) * pr.hq) * D + (((lane & 15) ^ (4 * (lane >> 4) + k)) << 3);
   auto load_tile = [&](int it, int buf) {
-    if (wu < 4) return;
+    if (wu < KG) return;
+    constexpr int HALF = KG / 2, PARTS = 16 / HALF;  // loading waves per tensor, parts each
+    const int r1 = wu - KG;
     const int h = kvh * g + it % g;
     const int r0 = tile_row(it);
-    const int p0 = (wu & 1) * 8;
-    const __bf16* base = wu < 6 ? pr.q : pr.dout;
-    __bf16* dst = wu < 6 ? &lq[buf][0] : &ldo[buf][0];
+    const int p0 = (r1 % HALF) * PARTS;
+    const __bf16* base = r1 < HALF ? pr.q : pr.dout;
+    __bf16* dst = r1 < HALF ? &lq[buf][0] : &ldo[buf][0];
     if (r0 + BQ <= s_q) {
 #pragma unroll
-      for (int pp = 0; pp < 8; ++pp) {
+      for (int pp = 0; pp < PARTS; ++pp) {
         const int part = p0 + pp;
         const __bf16* b = base + ((int64_t)(r0 + 4 * part) * pr.hq + h) * D;
         __builtin_amdgcn_global_load_lds(b + loff[part & 3], dst + part * 512, 16, 0, 0);
       }
     } else {  // the last tile: rows past the end read the last row (always masked)
 #pragma unroll
-      for (int pp = 0; pp < 8; ++pp) {
+      for (int pp = 0; pp < PARTS; ++pp) {
         const int part = p0 + pp;
         const int r = 4 * part + (lane >> 4), c = (lane & 15) ^ swz16(r);
         const int row = min(r0 + r, s_q - 1);
@@ -257,10 +267,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams pr) {
                                          dst + part * 512, 16, 0, 0);
       }
     }
-    if ((wu & 1) == 0) {
+    if (r1 % HALF == 0) {
       const int i = min(r0 + lane, s_q - 1);
-      const float* src = (wu == 4 ? pr.lse2 : pr.dd) + (int64_t)h * pr.s_tq + i;
-      float* sdst = wu == 4 ? &llse[buf][0] : &ldd[buf][0];
+      const float* src = (r1 == 0 ? pr.lse2 : pr.dd) + (int64_t)h * pr.s_tq + i;
+      float* sdst = r1 == 0 ? &llse[buf][0] : &ldd[buf][0];
       __builtin_amdgcn_global_load_lds(src, sdst, 4, 0, 0);
     }
   };
@@ -595,7 +605,8 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
 }
 
 constexpr int kDqKeys = DQ_KEYS;     // keys per dQ tile
-constexpr int kDkdvRows = DKDV_ROWS; // query rows per dK/dV tile
+constexpr int kDkdvRows = DKDV_ROWS;      // query rows per dK/dV tile
+constexpr int kDkdvGroups = DKDV_GROUPS;  // 32-key groups (wave pairs) per dK/dV workgroup
 
 template <int HG>
 int launch_dq(const BwdParams& p, int g, hipStream_t stream) {
@@ -652,9 +663,11 @@ int attn_bwd_bf16(const AttnArgs& a) {
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
   {
-    dim3 grid((unsigned)((a.s_k + 127) / 128), (unsigned)a.hkv);
+    constexpr int keys = 32 * kDkdvGroups;
+    dim3 grid((unsigned)((a.s_k + keys - 1) / keys), (unsigned)a.hkv);
     TraceScope ts("attn_bwd_dkdv_bf16", a.stream);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<kDkdvRows>), grid, dim3(512), 0, a.stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<kDkdvRows, kDkdvGroups>), grid, dim3(128 * kDkdvGroups), 0,
+                       a.stream, p);
     if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
   }
   const int g = a.hq / a.hkv;
