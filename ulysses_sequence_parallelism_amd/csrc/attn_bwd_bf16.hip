@@ -85,6 +85,35 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const __bf16* __restric
   }
 }
 
+// Direct global->LDS loads issued as inline asm (global_load_lds with a
+// scalar 64-bit base, a 32-bit lane offset and the LDS destination in M0).
+// The compiler does not see these as memory operations, so it neither waits
+// for them at every barrier nor in front of LDS reads it cannot tell apart
+// from the destination; the caller waits with vmcnt before the barrier that
+// publishes the data. Every direct load of a kernel that uses these must go
+// through them (M0 is written here behind the compiler's back).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ void wait_lds_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// LDS byte address of a pointer into a __shared__ array, made wave-uniform
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(p));
+}
+
 struct BwdParams {
   const __bf16* q;
   const __bf16* k;
@@ -237,10 +266,7 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
   // a lane offset; the swizzle makes the lane offsets repeat every 4 parts, so
   // they are computed once.
   const int wu = __builtin_amdgcn_readfirstlane(w);  // LDS destinations go to M0
-  int loff[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k)  // part = 4 p + k covers rows 16 p + 4 k + lane / 16
-    loff[k] = ((lane >> 4) * pr.hq) * D + (((lane & 15) ^ (4 * (lane >> 4) + k)) << 3);
+  const uint32_t row_bytes = (uint32_t)pr.hq * D * 2;
   auto load_tile = [&](int it, int buf) {
     if (wu < KG) return;
     constexpr int HALF = KG / 2, PARTS = 16 / HALF;  // loading waves per tensor, parts each
@@ -248,30 +274,33 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
     const int h = kvh * g + it % g;
     const int r0 = tile_row(it);
     const int p0 = (r1 % HALF) * PARTS;
-    const __bf16* base = r1 < HALF ? pr.q : pr.dout;
-    __bf16* dst = r1 < HALF ? &lq[buf][0] : &ldo[buf][0];
+    const char* base = reinterpret_cast<const char*>(r1 < HALF ? pr.q : pr.dout) + (int64_t)h * (D * 2);
+    const uint32_t dst = lds_addr(r1 < HALF ? &lq[buf][0] : &ldo[buf][0]);
+    // the lane's byte offset from the first row of a 4-row part: row lane / 16,
+    // swizzled chunk (the swizzle of row 4 p + q is 4 q + p % 4)
+    const uint32_t q = lane >> 4;
     if (r0 + BQ <= s_q) {
 #pragma unroll
       for (int pp = 0; pp < PARTS; ++pp) {
         const int part = p0 + pp;
-        const __bf16* b = base + ((int64_t)(r0 + 4 * part) * pr.hq + h) * D;
-        __builtin_amdgcn_global_load_lds(b + loff[part & 3], dst + part * 512, 16, 0, 0);
+        const uint32_t off = q * row_bytes + ((uint32_t)((lane & 15) ^ (4 * q + (part & 3))) << 4);
+        lds_dma16(base + (int64_t)(r0 + 4 * part) * row_bytes, off, dst + part * 1024);
       }
     } else {  // the last tile: rows past the end read the last row (always masked)
 #pragma unroll
       for (int pp = 0; pp < PARTS; ++pp) {
         const int part = p0 + pp;
-        const int r = 4 * part + (lane >> 4), c = (lane & 15) ^ swz16(r);
-        const int row = min(r0 + r, s_q - 1);
-        __builtin_amdgcn_global_load_lds(base + ((int64_t)row * pr.hq + h) * D + c * 8,
-                                         dst + part * 512, 16, 0, 0);
+        const int first = min(r0 + 4 * part, s_q - 1);
+        const uint32_t rel = (uint32_t)(min(r0 + 4 * part + (int)q, s_q - 1) - first);
+        const uint32_t off = rel * row_bytes + ((uint32_t)((lane & 15) ^ (4 * q + (part & 3))) << 4);
+        lds_dma16(base + (int64_t)first * row_bytes, off, dst + part * 1024);
       }
     }
     if (r1 % HALF == 0) {
-      const int i = min(r0 + lane, s_q - 1);
-      const float* src = (r1 == 0 ? pr.lse2 : pr.dd) + (int64_t)h * pr.s_tq + i;
-      float* sdst = r1 == 0 ? &llse[buf][0] : &ldd[buf][0];
-      __builtin_amdgcn_global_load_lds(src, sdst, 4, 0, 0);
+      const int i0 = min(r0, s_q - 1);
+      const uint32_t rel = (uint32_t)(min(r0 + lane, s_q - 1) - i0);
+      const float* src = (r1 == 0 ? pr.lse2 : pr.dd) + (int64_t)h * pr.s_tq + i0;
+      lds_dma4(src, rel * 4, lds_addr(r1 == 0 ? &llse[buf][0] : &ldd[buf][0]));
     }
   };
   // per-lane LDS element offsets of the row-fragment reads and of the
@@ -285,6 +314,7 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
     for (int h = 0; h < 2; ++h) troff[b][h] = tr_offset(lane, b, h);
 
   if (nt > 0) load_tile(0, 0);
+  wait_lds_dma();
   __syncthreads();
 
   for (int it = 0; it < nt; ++it) {
@@ -400,7 +430,8 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
           for (int bb = 0; bb < 2; ++bb) acc[b2 + bb] = mfma32(af[bb][ch], pb[ch], acc[b2 + bb]);
       }
     }
-    __syncthreads();  // also waits for the next tile's loads
+    wait_lds_dma();  // the next tile has landed (only the loading waves wait)
+    __syncthreads();
   }
 
   if (key < s_k)
