@@ -504,37 +504,25 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
   const int nt = kmax >= kmin ? (kmax - tstart) / BN + 1 : 0;
 
   // 16 wave-loads of 1 KiB per tile, 4 per wave: wave w brings K and V parts
-  // 2w, 2w+1 (4 keys each). A load's address is a wave-uniform base plus a
-  // lane offset.
+  // 2w, 2w+1 (4 keys each), as inline-asm direct loads (see lds_dma16): a
+  // wave-uniform base plus a 32-bit lane offset.
   const int wu = __builtin_amdgcn_readfirstlane(w);  // LDS destinations go to M0
-  int kvoff[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int rr = 4 * (lane >> 4) + ((2 * wu + j) & 3);  // swz16 of the row
-    kvoff[j] = ((lane >> 4) * pr.hkv) * D + (((lane & 15) ^ rr) << 3);
-  }
+  const uint32_t key_bytes = (uint32_t)pr.hkv * D * 2;
   auto load_tile = [&](int t0, int buf) {
-    // (through local pointers: naming the shared arrays inside the builtin
-    // calls makes the host pass silently drop this kernel's launch stub)
-    __bf16* dk_ = buf ? &lk1[0] : &lk0[0];
-    __bf16* dv_ = buf ? &lv1[0] : &lv0[0];
-    if (t0 + BN <= s_k) {
+    const uint32_t dk = lds_addr(buf ? &lk1[0] : &lk0[0]);
+    const uint32_t dv = lds_addr(buf ? &lv1[0] : &lv0[0]);
+    const char* kb = reinterpret_cast<const char*>(pr.k) + (int64_t)kvh * (D * 2);
+    const char* vb = reinterpret_cast<const char*>(pr.v) + (int64_t)kvh * (D * 2);
+    const uint32_t q = lane >> 4;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int part = 2 * wu + j;
-        const int64_t rowoff = ((int64_t)(t0 + 4 * part) * pr.hkv + kvh) * D;
-        __builtin_amdgcn_global_load_lds(pr.k + rowoff + kvoff[j], dk_ + part * 512, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(pr.v + rowoff + kvoff[j], dv_ + part * 512, 16, 0, 0);
-      }
-    } else {  // keys past the end read the last key (always masked)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int part = 2 * wu + j;
-        const int r = 4 * part + (lane >> 4), c = (lane & 15) ^ swz16(r);
-        const int64_t off = ((int64_t)min(t0 + r, s_k - 1) * pr.hkv + kvh) * D + c * 8;
-        __builtin_amdgcn_global_load_lds(pr.k + off, dk_ + part * 512, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(pr.v + off, dv_ + part * 512, 16, 0, 0);
-      }
+    for (int j = 0; j < 2; ++j) {
+      const int part = 2 * wu + j;
+      // keys past the end read the last key (always masked)
+      const int first = min(t0 + 4 * part, s_k - 1);
+      const uint32_t rel = (uint32_t)(min(t0 + 4 * part + (int)q, s_k - 1) - first);
+      const uint32_t off = rel * key_bytes + ((uint32_t)((lane & 15) ^ (4 * q + (part & 3))) << 4);
+      lds_dma16(kb + (int64_t)first * key_bytes, off, dk + part * 1024);
+      lds_dma16(vb + (int64_t)first * key_bytes, off, dv + part * 1024);
     }
   };
   // fragment read offsets (elements) within a tile
@@ -547,6 +535,7 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
     for (int h = 0; h < 2; ++h) troff[b][h] = tr_offset(lane, b, h);
 
   if (nt > 0) load_tile(tstart, 0);
+  wait_lds_dma();
   __syncthreads();
 
   auto step = [&](int it, auto parity) {
@@ -623,7 +612,8 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
           for (int b = 0; b < 4; ++b) dqa[b] = mfma32(af[b][ch], dst[ch], dqa[b]);
       }
     }
-    __syncthreads();  // also waits for the next tile's loads
+    wait_lds_dma();  // the next tile has landed
+    __syncthreads();
   };
   for (int it = 0; it < nt; it += 2) {
     step(it, std::integral_constant<int, 0>{});
