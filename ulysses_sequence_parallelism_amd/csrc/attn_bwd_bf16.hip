@@ -85,35 +85,6 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const __bf16* __restric
   }
 }
 
-// Direct global->LDS loads issued as inline asm (global_load_lds with a
-// scalar 64-bit base, a 32-bit lane offset and the LDS destination in M0).
-// The compiler does not see these as memory operations, so it neither waits
-// for them at every barrier nor in front of LDS reads it cannot tell apart
-// from the destination; the caller waits with vmcnt before the barrier that
-// publishes the data. Every direct load of a kernel that uses these must go
-// through them (M0 is written here behind the compiler's back).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-__device__ __forceinline__ void wait_lds_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// LDS byte address of a pointer into a __shared__ array, made wave-uniform
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(p));
-}
-
 struct BwdParams {
   const __bf16* q;
   const __bf16* k;

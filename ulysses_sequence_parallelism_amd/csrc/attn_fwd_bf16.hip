@@ -148,44 +148,36 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
   // K(t+2) goes into K(t)'s slot and V(t+1) into V(t-1)'s (both last read in
   // step t-1), so each needs two slots and there is one barrier per tile.
   // Wave w loads K parts 2w, 2w+1 (4 keys each) and V^T parts 2w, 2w+1 (8
-  // d-rows each); a load's address is a wave-uniform base plus a lane offset.
+  // d-rows each) as inline-asm direct loads (lds_dma16): a wave-uniform base
+  // plus a 32-bit lane offset.
   const int wu = __builtin_amdgcn_readfirstlane(w);  // LDS destinations go to M0
-  int koff[2], voff[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int rr = 4 * ((2 * wu + j) & 3) + (lane >> 4);  // key row within 16
-    koff[j] = ((lane >> 4) * pr.hkv) * D + (((lane & 15) ^ rr) << 3);
-    voff[j] = (lane >> 3) * (int)pr.s_t + (((lane & 7) ^ (4 * j + (lane >> 4))) << 3);
-  }
+  const uint32_t key_bytes = (uint32_t)pr.hkv * D * 2;
+  const uint32_t vt_row_bytes = (uint32_t)pr.s_t * 2;
   auto load_k = [&](int t, int slot) {
     const int t0 = tstart + t * BN;
-    __bf16* dst = kslot(slot);  // (a local pointer: see the dQ kernel)
-    if (t0 + BN <= s_k) {
+    const uint32_t dst = lds_addr(kslot(slot));
+    const char* kb = reinterpret_cast<const char*>(pr.k) + (int64_t)kvh * (D * 2);
+    const uint32_t q = lane >> 4;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int part = 2 * wu + j;
-        const __bf16* b = pr.k + ((int64_t)(t0 + 4 * part) * pr.hkv + kvh) * D;
-        __builtin_amdgcn_global_load_lds(b + koff[j], dst + part * 512, 16, 0, 0);
-      }
-    } else {  // keys past the end read the last key (always masked)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int part = 2 * wu + j;
-        const int r = 4 * part + (lane >> 4), c = (lane & 15) ^ (r & 15);
-        const int key = min(t0 + r, s_k - 1);
-        __builtin_amdgcn_global_load_lds(pr.k + ((int64_t)key * pr.hkv + kvh) * D + c * 8,
-                                         dst + part * 512, 16, 0, 0);
-      }
+    for (int j = 0; j < 2; ++j) {
+      const int part = 2 * wu + j;
+      // keys past the end read the last key (always masked)
+      const int first = min(t0 + 4 * part, s_k - 1);
+      const uint32_t rel = (uint32_t)(min(t0 + 4 * part + (int)q, s_k - 1) - first);
+      const uint32_t off = rel * key_bytes + ((uint32_t)((lane & 15) ^ (4 * (part & 3) + q)) << 4);
+      lds_dma16(kb + (int64_t)first * key_bytes, off, dst + part * 1024);
     }
   };
   auto load_v = [&](int t, int slot) {
     const int t0 = tstart + t * BN;
-    __bf16* dst = vslot(slot);
+    const uint32_t dst = lds_addr(vslot(slot));
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int part = 2 * wu + j;
-      const __bf16* b = pr.vt + ((int64_t)kvh * D + 8 * part) * pr.s_t + t0;
-      __builtin_amdgcn_global_load_lds(b + voff[j], dst + part * 512, 16, 0, 0);
+      const char* b = reinterpret_cast<const char*>(pr.vt + ((int64_t)kvh * D + 8 * part) * pr.s_t + t0);
+      const uint32_t off = (uint32_t)(lane >> 3) * vt_row_bytes +
+                           ((uint32_t)((lane & 7) ^ (4 * j + (lane >> 4))) << 4);
+      lds_dma16(b, off, dst + part * 1024);
     }
   };
   // fragment read offsets (elements) within a tile
@@ -214,6 +206,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
     if (nt > 1) load_k(1, 1);
     load_v(0, 0);
   }
+  wait_lds_dma();
   __syncthreads();
   if (nt > 0) scores(0, sa);
   __syncthreads();  // S(0) is read from slot 0 before iteration 0 refills it
@@ -293,7 +286,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
         }
       }
 
-      __syncthreads();  // also waits for this step's loads
+      wait_lds_dma();  // this step's loads have landed
+      __syncthreads();
   };
   for (int it = 0; it < nt; it += 2) {
     step(it, sa, sb, std::integral_constant<int, 0>{});
