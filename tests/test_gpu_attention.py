@@ -51,6 +51,12 @@ SMALL = [
     ("docs_16q4kv", 2048, 2048, 16, 4, [0, 700, 1300, 2048], True),
     ("bidirectional_padded", 500, 490, 4, 1, None, False),
     ("bidirectional_docs", 600, 600, 4, 2, [0, 250, 600], False),
+    # shorter than one 32-row block: every tile is a ragged tail
+    ("tiny_1", 1, 1, 4, 1, None, True),
+    ("tiny_17", 17, 17, 4, 1, None, True),
+    ("tiny_bidir_33", 33, 30, 4, 2, None, False),
+    # 8 query heads per KV head: two head chunks per KV head
+    ("gqa8", 300, 300, 8, 1, None, True),
 ]
 
 
