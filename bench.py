@@ -397,18 +397,21 @@ def main():
     # ---- timed region: K steps, kernel trace on
     usp.usp_trace_enable(True)
     usp.usp_trace_collect()  # drop anything recorded before
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event per step boundary on the current stream: the mean over the K
+    # steps is the reported step time, the median and minimum go alongside
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
+    evs[0].record()
+    for i in range(args.steps):
         step()
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     usp.usp_trace_enable(False)
     trace = usp.usp_trace_collect()
-    step_ms = ev0.elapsed_time(ev1) / args.steps
+    step_ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
 
     pairs = causal_pairs(w.s_pad) if w.s == w.s_pad else causal_pairs(w.s) + (w.s_pad - w.s) * w.s
     f_fwd = 4 * d * hq * pairs
@@ -463,6 +466,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(step_ms, 3),
+        "ms_per_step_median": round(per_step[len(per_step) // 2], 3),
+        "ms_per_step_min": round(per_step[0], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
