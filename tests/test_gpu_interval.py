@@ -58,6 +58,9 @@ CASES = [
     ("cp_docs", 1200, 1200, 8, 2, [0, 300, 701, 1200], [0, 1200], [0, 333, 900, 1200], True),
     ("bidir_padded", 900, 890, 4, 2, [0, 900], [0, 300, 600, 900], None, False),
     ("bidir_grid_docs", 640, 640, 4, 1, [0, 200, 640], [0, 320, 640], [0, 250, 640], False),
+    # one-row query interval, one-key and two-key key intervals
+    ("single_rows", 70, 70, 4, 1, [0, 1, 70], [0, 1, 3, 70], None, True),
+    ("single_rows_bidir", 70, 66, 4, 2, [0, 1, 69, 70], [0, 1, 3, 70], None, False),
 ]
 
 
