@@ -285,6 +285,16 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
           oacc[b] = mfma32(*reinterpret_cast<const bf16x8*>(vp + vro[ch]), pb[ch], oacc[b]);
         }
       }
+      // Instruction order for this block: fragment reads run four ahead of
+      // the MFMAs that consume them (otherwise each MFMA waits on a read
+      // issued just before it), and the softmax work fills the score MFMAs'
+      // shadows.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+      }
 
       wait_lds_dma();  // this step's loads have landed
       __syncthreads();
