@@ -523,19 +523,27 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
         // the A fragments of each chain are requested before the chain runs
         const __bf16* kp = (buf ? &lk1[0] : &lk0[0]) + kb * 32 * D;
         const __bf16* vp = (buf ? &lv1[0] : &lv0[0]) + kb * 32 * D;
-        bf16x8 af[8];
+        bf16x8 afk[8], afv[8];
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) af[kk] = *reinterpret_cast<const bf16x8*>(kp + kro[kk]);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int kk = 0; kk < 8; ++kk) afk[kk] = *reinterpret_cast<const bf16x8*>(kp + kro[kk]);
         sa[kb] = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) sa[kb] = mfma32(af[kk], qreg[kk], sa[kb]);
+        for (int kk = 0; kk < 8; ++kk) sa[kb] = mfma32(afk[kk], qreg[kk], sa[kb]);
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) af[kk] = *reinterpret_cast<const bf16x8*>(vp + kro[kk]);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int kk = 0; kk < 8; ++kk) afv[kk] = *reinterpret_cast<const bf16x8*>(vp + kro[kk]);
         pa[kb] = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) pa[kb] = mfma32(af[kk], doreg[kk], pa[kb]);
+        for (int kk = 0; kk < 8; ++kk) pa[kb] = mfma32(afv[kk], doreg[kk], pa[kb]);
+        // Order: the 8 K fragments, then the S chain with one V fragment read
+        // after each of its MFMAs (the V reads overlap the chain instead of
+        // starting after it), then the dP chain.
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // 8 LDS reads (K)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA (S)
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read (V)
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // the dP chain
       }
       const bool full = t0 >= free_lo && t0 + BN - 1 <= free_hi;
       // dS^T = P^T (dP^T - D); most tiles need no mask, so the mask test is
