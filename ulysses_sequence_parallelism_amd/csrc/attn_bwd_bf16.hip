@@ -385,21 +385,28 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
       }
       // dO^T (role 0) or Q^T (role 1): transposed reads of the row tile
       const __bf16* tbase = role == 0 ? tdo : tq;
+      bf16x8 af[4][NCH];
 #pragma unroll
       for (int b2 = 0; b2 < 4; b2 += 2) {
-        // fragments of two output blocks requested together (see above)
-        bf16x8 af[2][NCH];
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
           for (int ch = 0; ch < NCH; ++ch)
-            af[bb][ch] = frag_tr(tbase + ch * 16 * D, troff[b2 + bb][0], troff[b2 + bb][1]);
-        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the chain
+            af[b2 + bb][ch] = frag_tr(tbase + ch * 16 * D, troff[b2 + bb][0], troff[b2 + bb][1]);
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
-          for (int bb = 0; bb < 2; ++bb) acc[b2 + bb] = mfma32(af[bb][ch], pb[ch], acc[b2 + bb]);
+          for (int bb = 0; bb < 2; ++bb) acc[b2 + bb] = mfma32(af[b2 + bb][ch], pb[ch], acc[b2 + bb]);
       }
+      // Order: the first pair's 16 transposed reads, then its chain with two
+      // of the second pair's reads after each MFMA, then the second chain.
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
     wait_lds_dma();  // the next tile has landed (only the loading waves wait)
     __syncthreads();
