@@ -553,6 +553,17 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // the dP chain
       }
       const bool full = t0 >= free_lo && t0 + BN - 1 <= free_hi;
+      // K^T fragments for dQ^T += K^T dS^T, requested before the softmax so
+      // that its vector work covers their latency
+      bf16x8 kft[4][2 * KB];
+      {
+        const __bf16* kt = buf ? &lk1[0] : &lk0[0];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int ch = 0; ch < 2 * KB; ++ch)
+            kft[b][ch] = frag_tr(kt + ch * 16 * D, troff[b][0], troff[b][1]);
+      }
       // dS^T = P^T (dP^T - D); most tiles need no mask, so the mask test is
       // kept off their path
       auto dsoft = [&](auto masked) {
@@ -583,20 +594,10 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
         }
       }
       // dQ^T += K^T dS^T (rows = d, cols = queries)
-      {
-        bf16x8 af[4][2 * KB];
-        const __bf16* kt = buf ? &lk1[0] : &lk0[0];
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+      for (int ch = 0; ch < 2 * KB; ++ch)
 #pragma unroll
-          for (int ch = 0; ch < 2 * KB; ++ch)
-            af[b][ch] = frag_tr(kt + ch * 16 * D, troff[b][0], troff[b][1]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ch = 0; ch < 2 * KB; ++ch)
-#pragma unroll
-          for (int b = 0; b < 4; ++b) dqa[b] = mfma32(af[b][ch], dst[ch], dqa[b]);
-      }
+        for (int b = 0; b < 4; ++b) dqa[b] = mfma32(kft[b][ch], dst[ch], dqa[b]);
     }
     wait_lds_dma();  // the next tile has landed
     __syncthreads();
