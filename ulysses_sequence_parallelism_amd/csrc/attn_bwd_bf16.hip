@@ -230,12 +230,13 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
   // One tile = Q and dO (64 rows x 256 B: 32 wave-loads of 1 KiB) plus the
   // 64 LSE and D values. Rows past the end read the last row: every load is
   // unconditional and such rows are always masked. The next tile is loaded at
-  // the top of each tile by the role-1 waves, whose first phase is the shorter
-  // one: the first half of them bring Q, the second half dO (16 parts of 4
-  // rows each, split evenly), and the first wave of each half also the LSE or
-  // D of the tile's rows. The address of each load is a wave-uniform base plus
-  // a lane offset; the swizzle makes the lane offsets repeat every 4 parts, so
-  // they are computed once.
+  // the top of each tile by the role-1 waves (issuing stalls a wave while the
+  // CU's load path drains the burst, and their first phase has the slack): the
+  // first half of them bring Q, the second half dO (16 parts of 4 rows each,
+  // split evenly), and the first wave of each half also the LSE or D of the
+  // tile's rows. Each load is an inline-asm direct load (lds_dma16): a
+  // wave-uniform 64-bit base plus a 32-bit lane offset formed per load, waited
+  // for once before the barrier that ends the tile.
   const int wu = __builtin_amdgcn_readfirstlane(w);  // LDS destinations go to M0
   const uint32_t row_bytes = (uint32_t)pr.hq * D * 2;
   auto load_tile = [&](int it, int buf) {
