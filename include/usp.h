@@ -111,7 +111,7 @@ size_t usp_attn_fwd_workspace_bytes(int64_t s_pad, int hq, int hkv, int d, int d
  *     outside [0, s_pad] are clamped, never dereferenced out of range.
  *   workspace: device memory of usp_attn_fwd_workspace_bytes() bytes (may be
  *     NULL when that is 0); contents are scratch.
- * Supported: d in {64, 128} for USP_FP32, d = 128 for USP_BF16.
+ * Supported: d in {64, 128}, both dtypes.
  * Errors: USP_ERR_INVALID for s_valid < 1 or > s_pad, hq % hkv != 0,
  * cu_seqlens with s_valid != s_pad or n_docs < 1, misalignment, aliasing;
  * USP_ERR_UNSUPPORTED for other d / dtype; USP_ERR_WORKSPACE if the workspace

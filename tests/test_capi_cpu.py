@@ -120,7 +120,8 @@ def test_attention_argument_errors(L, f):
     assert f(L, cu=A + (8 << 24), n_docs=2, s_valid=250) == INVALID  # packed docs + padding
     assert f(L, cu=A + (8 << 24), n_docs=0) == INVALID
     assert f(L, cu=A + (8 << 24) + 2, n_docs=2) == INVALID            # misaligned offsets
-    assert f(L, d=64) == UNSUPPORTED                    # bf16 is built for d = 128
+    assert f(L, d=96) == UNSUPPORTED                    # head dims 64 and 128 are built
+    assert f(L, d=32) == UNSUPPORTED
     assert f(L, d=96, dt=FP32) == UNSUPPORTED
     assert f(L, dt=3) == UNSUPPORTED
     assert f(L, scale=0.0) == INVALID
@@ -179,7 +180,7 @@ def test_interval_argument_errors(L, f):
     assert f(L, hq=6, hkv=4) == INVALID
     assert f(L, cu=A + (8 << 24), n_docs=0) == INVALID
     assert f(L, cu=A + (8 << 24) + 2, n_docs=2) == INVALID
-    assert f(L, d=64) == UNSUPPORTED
+    assert f(L, d=96) == UNSUPPORTED
     assert f(L, dt=3) == UNSUPPORTED
     assert f(L, scale=-1.0) == INVALID
     assert f(L, causal=-1) == INVALID

@@ -57,15 +57,22 @@ SMALL = [
     ("tiny_bidir_33", 33, 30, 4, 2, None, False),
     # 8 query heads per KV head: two head chunks per KV head
     ("gqa8", 300, 300, 8, 1, None, True),
+    # head dim 64 (128-byte rows: their own tile swizzle and load mapping)
+    ("d64_ragged", 300, 300, 4, 1, None, True, 64),
+    ("d64_padded_gqa2", 1000, 997, 4, 2, None, True, 64),
+    ("d64_mha", 513, 513, 2, 2, None, True, 64),
+    ("d64_docs", 2100, 2100, 4, 1, [0, 100, 101, 1000, 1377, 2100], True, 64),
+    ("d64_bidir_padded", 500, 490, 8, 2, None, False, 64),
+    ("d64_tiny_17", 17, 17, 4, 1, None, True, 64),
 ]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_bf16_small_full_compare(case):
-    name, s, s_valid, hq, hkv, cu, causal = case
+    name, s, s_valid, hq, hkv, cu, causal = case[:7]
+    d = case[7] if len(case) > 7 else 128
     dev = gpu()
-    say(f"bf16 {name}: S={s} s_valid={s_valid} hq={hq} hkv={hkv} causal={causal}")
-    d = 128
+    say(f"bf16 {name}: S={s} s_valid={s_valid} hq={hq} hkv={hkv} d={d} causal={causal}")
     q, k, v, do = (seeded((s, h, d), 1000 + i, torch.bfloat16)
                    for i, h in enumerate((hq, hkv, hkv, hq)))
     if s_valid < s:  # pack zero-fills padded rows

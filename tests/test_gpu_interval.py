@@ -61,6 +61,11 @@ CASES = [
     # one-row query interval, one-key and two-key key intervals
     ("single_rows", 70, 70, 4, 1, [0, 1, 70], [0, 1, 3, 70], None, True),
     ("single_rows_bidir", 70, 66, 4, 2, [0, 1, 69, 70], [0, 1, 3, 70], None, False),
+    # head dim 64
+    ("d64_usp_grid", 900, 900, 4, 2, [0, 333, 900], [0, 100, 450, 900], None, True, 64),
+    ("d64_cp_docs", 1200, 1200, 8, 2, [0, 300, 701, 1200], [0, 1200], [0, 333, 900, 1200], True,
+     64),
+    ("d64_bidir_padded", 900, 890, 4, 1, [0, 900], [0, 300, 600, 900], None, False, 64),
 ]
 
 
@@ -70,12 +75,12 @@ def test_bf16_interval_split_forward_backward(case):
     merge forward partials over the key intervals, accumulate dQ over the key
     intervals and dK / dV over the query intervals; compare partials and
     totals with the oracle."""
-    name, s, s_valid, hq, hkv, qe, ke, cu, causal = case
+    name, s, s_valid, hq, hkv, qe, ke, cu, causal = case[:9]
+    d = case[9] if len(case) > 9 else 128
     L = usp()
     dev = gpu()
-    d = 128
     scale = d ** -0.5
-    say(f"interval {name}: S={s} hq={hq} hkv={hkv} q={qe} k={ke} causal={causal}")
+    say(f"interval {name}: S={s} hq={hq} hkv={hkv} d={d} q={qe} k={ke} causal={causal}")
     q, k, v, do = (seeded((s, h, d), 5000 + i, torch.bfloat16)
                    for i, h in enumerate((hq, hkv, hkv, hq)))
     if s_valid < s:

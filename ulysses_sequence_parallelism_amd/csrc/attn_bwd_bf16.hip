@@ -1,4 +1,4 @@
-// Attention backward, bf16 in / fp32 accumulate, d = 128, gfx950 matrix cores.
+// Attention backward, bf16 in / fp32 accumulate, d = 128 or 64, gfx950 matrix cores.
 //
 // Gradients of one rank's local attention ("feat(dspark): add Ulysses sequence
 // parallel training", Accuracy Test: loss and gradient parity with full-sequence
@@ -52,19 +52,19 @@ namespace usp {
 
 namespace {
 
-constexpr int D = 128;
-
 // ---------------------------------------------------------------------------
 // D_i = sum_d dO[i][h][d] * O[i][h][d]  (fp32 from the bf16 values)
+template <int D>
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const __bf16* __restrict__ o,
                                                          const __bf16* __restrict__ dout,
                                                          const float* __restrict__ lse,
                                                          float* __restrict__ dd,
                                                          float* __restrict__ lse2, int s_q,
                                                          int hq, int64_t s_t) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 16 lanes per (row, head)
-  const int64_t rh = t >> 4;
-  const int part = (int)(t & 15);
+  constexpr int LPR = D / 8;  // lanes per (row, head), 8 elements each
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rh = t / LPR;
+  const int part = (int)(t % LPR);
   float s = 0.f;
   const bool live = rh < (int64_t)s_q * hq;
   if (live) {
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const __bf16* __restric
     }
   }
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 16);
+  for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, LPR);
   if (live && part == 0) {
     const int i = (int)(rh / hq), h = (int)(rh % hq);
     dd[(int64_t)h * s_t + i] = s;
@@ -103,15 +103,16 @@ struct BwdParams {
   float scale, scale_log2;
 };
 
-// Write 4 x 4 accumulator values (registers 4r..4r+3 of block b go to
+// Write DB x 4 accumulator values (registers 4r..4r+3 of block b go to
 // elements b*32 + r*8 + [0, 4) past p) scaled by f, as bf16, as fp32, or added
 // to fp32.
-__device__ __forceinline__ void store_rows(void* out, int64_t off, const f32x16 (&acc)[4],
+template <int DB>
+__device__ __forceinline__ void store_rows(void* out, int64_t off, const f32x16 (&acc)[DB],
                                            float f, int f32, int accum) {
   if (f32) {
     float* p = static_cast<float*>(out) + off;
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         f32x4 v4 = {acc[b][4 * r] * f, acc[b][4 * r + 1] * f, acc[b][4 * r + 2] * f,
@@ -123,7 +124,7 @@ __device__ __forceinline__ void store_rows(void* out, int64_t off, const f32x16 
   } else {
     __bf16* p = static_cast<__bf16*>(out) + off;
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         u32x2 v2 = {pack_bf16x2(acc[b][4 * r] * f, acc[b][4 * r + 1] * f),
@@ -150,14 +151,18 @@ __device__ __forceinline__ void store_rows(void* out, int64_t off, const f32x16 
 // Q and dO tiles go from global memory straight into LDS
 // (global_load_lds_dwordx4: no staging registers, no LDS stores). That load
 // writes each lane's 16 bytes at consecutive LDS addresses, so rows cannot be
-// padded; instead chunk c of a 256-byte row r sits in slot c ^ swz16(r). The
+// padded; instead chunk c of row r sits in slot c ^ swz_row(r). The
 // phase-1 operands (Q, dO with rows = queries) are read as row fragments; the
 // phase-2 operands (Q^T, dO^T with rows = d) are read from the same tiles with
 // transposed LDS reads, in the row order in which P and dS leave the
 // accumulators. Both read patterns are conflict-free under swz16.
-template <int BQ, int KG>
+template <int D, int BQ, int KG>
 __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(BwdParams pr) {
   static_assert(KG == 2 || KG == 4, "2 or 4 key groups per workgroup");
+  constexpr int KK = D / 16;    // 16-wide reduction steps over d
+  constexpr int DB = D / 32;    // 32-row blocks of dK^T / dV^T
+  constexpr int KC = D / 8;     // 16-byte chunks per tile row
+  constexpr int RPP = 64 / KC;  // tile rows per 1 KiB wave-load
   constexpr int KEYS = 32 * KG;        // keys per workgroup
   static_assert(BQ == 64, "the direct-load tile mapping assumes 64-row tiles");
   constexpr int MB = BQ / 32;          // 32-row blocks per tile
@@ -202,20 +207,20 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
   const int wr_hi = key_rows(pr.m, min(wj0 + 31, s_k - 1)).hi - 1;
 
   // stationary fragment (B operand, lane = key): K for role 0, V for role 1
-  bf16x8 sreg[8];
+  bf16x8 sreg[KK];
   {
     const __bf16* src = role == 0 ? pr.k : pr.v;
     const int64_t off = ((int64_t)kc * pr.hkv + kvh) * D + hl * 8;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) sreg[kk] = *reinterpret_cast<const bf16x8*>(src + off + kk * 16);
+    for (int kk = 0; kk < KK; ++kk) sreg[kk] = *reinterpret_cast<const bf16x8*>(src + off + kk * 16);
   }
   // Retire the stationary loads here; otherwise the wait-count pass treats
   // them as possibly in flight inside the loop and makes every MFMA wait for
   // the next tile's loads too.
   __builtin_amdgcn_s_waitcnt(0);
-  f32x16 acc[4];  // dV^T (role 0) or dK^T (role 1): rows = d, cols = keys
+  f32x16 acc[DB];  // dV^T (role 0) or dK^T (role 1): rows = d, cols = keys
 #pragma unroll
-  for (int b = 0; b < 4; ++b) acc[b] = f32x16{};
+  for (int b = 0; b < DB; ++b) acc[b] = f32x16{};
 
   const int tstart = (rstart / BQ) * BQ;
   const int ntr = (j0 < s_kv && rend >= rstart) ? (rend - tstart) / BQ + 1 : 0;
@@ -227,44 +232,46 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
   // tiles are shared through L2 instead of each workgroup streaming its own
   // row range.
   auto tile_row = [&](int it) { return tstart + (ntr - 1 - it / g) * BQ; };
-  // One tile = Q and dO (64 rows x 256 B: 32 wave-loads of 1 KiB) plus the
-  // 64 LSE and D values. Rows past the end read the last row: every load is
-  // unconditional and such rows are always masked. The next tile is loaded at
-  // the top of each tile by the role-1 waves (issuing stalls a wave while the
-  // CU's load path drains the burst, and their first phase has the slack): the
-  // first half of them bring Q, the second half dO (16 parts of 4 rows each,
-  // split evenly), and the first wave of each half also the LSE or D of the
-  // tile's rows. Each load is an inline-asm direct load (lds_dma16): a
+  // One tile = Q and dO (64 rows x 2d bytes: 64 / RPP wave-loads of 1 KiB,
+  // RPP rows each, per tensor) plus the 64 LSE and D values. Rows past the end
+  // read the last row: every load is unconditional and such rows are always
+  // masked. The next tile is loaded at the top of each tile by the role-1 waves
+  // (issuing stalls a wave while the CU's load path drains the burst, and their
+  // first phase has the slack): the first half of them bring Q, the second half
+  // dO (the parts split evenly), and the first wave of each half also the LSE
+  // or D of the tile's rows. Each load is an inline-asm direct load (lds_dma16): a
   // wave-uniform 64-bit base plus a 32-bit lane offset formed per load, waited
   // for once before the barrier that ends the tile.
   const int wu = __builtin_amdgcn_readfirstlane(w);  // LDS destinations go to M0
   const uint32_t row_bytes = (uint32_t)pr.hq * D * 2;
   auto load_tile = [&](int it, int buf) {
     if (wu < KG) return;
-    constexpr int HALF = KG / 2, PARTS = 16 / HALF;  // loading waves per tensor, parts each
+    constexpr int HALF = KG / 2, PARTS = BQ / RPP / HALF;  // loading waves per tensor, parts each
     const int r1 = wu - KG;
     const int h = kvh * g + it % g;
     const int r0 = tile_row(it);
     const int p0 = (r1 % HALF) * PARTS;
     const char* base = reinterpret_cast<const char*>(r1 < HALF ? pr.q : pr.dout) + (int64_t)h * (D * 2);
     const uint32_t dst = lds_addr(r1 < HALF ? &lq[buf][0] : &ldo[buf][0]);
-    // the lane's byte offset from the first row of a 4-row part: row lane / 16,
-    // swizzled chunk (the swizzle of row 4 p + q is 4 q + p % 4)
-    const uint32_t q = lane >> 4;
+    // the lane's byte offset from the first row of a part: row lane / KC,
+    // swizzled chunk
+    const int q = lane / KC;
     if (r0 + BQ <= s_q) {
 #pragma unroll
       for (int pp = 0; pp < PARTS; ++pp) {
         const int part = p0 + pp;
-        const uint32_t off = q * row_bytes + ((uint32_t)((lane & 15) ^ (4 * q + (part & 3))) << 4);
-        lds_dma16(base + (int64_t)(r0 + 4 * part) * row_bytes, off, dst + part * 1024);
+        const uint32_t off =
+            (uint32_t)q * row_bytes + ((uint32_t)((lane % KC) ^ swz_row<D>(RPP * part + q)) << 4);
+        lds_dma16(base + (int64_t)(r0 + RPP * part) * row_bytes, off, dst + part * 1024);
       }
     } else {  // the last tile: rows past the end read the last row (always masked)
 #pragma unroll
       for (int pp = 0; pp < PARTS; ++pp) {
         const int part = p0 + pp;
-        const int first = min(r0 + 4 * part, s_q - 1);
-        const uint32_t rel = (uint32_t)(min(r0 + 4 * part + (int)q, s_q - 1) - first);
-        const uint32_t off = rel * row_bytes + ((uint32_t)((lane & 15) ^ (4 * q + (part & 3))) << 4);
+        const int first = min(r0 + RPP * part, s_q - 1);
+        const uint32_t rel = (uint32_t)(min(r0 + RPP * part + q, s_q - 1) - first);
+        const uint32_t off =
+            rel * row_bytes + ((uint32_t)((lane % KC) ^ swz_row<D>(RPP * part + q)) << 4);
         lds_dma16(base + (int64_t)first * row_bytes, off, dst + part * 1024);
       }
     }
@@ -277,13 +284,13 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
   };
   // per-lane LDS element offsets of the row-fragment reads and of the
   // transposed reads (column block b, half h) within a tile
-  int roff[8], troff[4][2];
+  int roff[KK], troff[DB][2];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) roff[kk] = ln * D + (((hl + 2 * kk) ^ swz16(ln)) << 3);
+  for (int kk = 0; kk < KK; ++kk) roff[kk] = ln * D + (((hl + 2 * kk) ^ swz_row<D>(ln)) << 3);
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int b = 0; b < DB; ++b)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) troff[b][h] = tr_offset(lane, b, h);
+    for (int h = 0; h < 2; ++h) troff[b][h] = tr_offset<D>(lane, b, h);
 
   if (nt > 0) load_tile(0, 0);
   wait_lds_dma();
@@ -311,13 +318,13 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
         // all 8 A fragments of the block are requested before its MFMA chain,
         // so the chain waits for one LDS round trip, not one per MFMA pair
         const __bf16* ap = base + mb * 32 * D;
-        bf16x8 af[8];
+        bf16x8 af[KK];
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) af[kk] = *reinterpret_cast<const bf16x8*>(ap + roff[kk]);
+        for (int kk = 0; kk < KK; ++kk) af[kk] = *reinterpret_cast<const bf16x8*>(ap + roff[kk]);
         __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the chain
         pa[mb] = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) pa[mb] = mfma32(af[kk], sreg[kk], pa[mb]);
+        for (int kk = 0; kk < KK; ++kk) pa[mb] = mfma32(af[kk], sreg[kk], pa[mb]);
       }
       if (role == 0) {
         // P = exp2(S*scale*log2e - LSE*log2e); masked entries are 0. Most
@@ -386,9 +393,9 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
       }
       // dO^T (role 0) or Q^T (role 1): transposed reads of the row tile
       const __bf16* tbase = role == 0 ? tdo : tq;
-      bf16x8 af[4][NCH];
+      bf16x8 af[DB][NCH];
 #pragma unroll
-      for (int b2 = 0; b2 < 4; b2 += 2) {
+      for (int b2 = 0; b2 < DB; b2 += 2) {
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
@@ -402,10 +409,12 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
       // Order: the first pair's 16 transposed reads, then its chain with two
       // of the second pair's reads after each MFMA, then the second chain.
       __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+      if constexpr (DB == 4) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
@@ -414,7 +423,7 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
   }
 
   if (key < s_k)
-    store_rows(role == 0 ? pr.dv : pr.dk, ((int64_t)key * pr.hkv + kvh) * D + hl * 4, acc,
+    store_rows<DB>(role == 0 ? pr.dv : pr.dk, ((int64_t)key * pr.hkv + kvh) * D + hl * 4, acc,
                role == 0 ? 1.f : pr.scale, pr.grad_f32, pr.accum);
 }
 
@@ -426,9 +435,14 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
 // K and V tiles go straight from global memory into LDS with the dK/dV
 // kernel's row swizzle; K^T for dQ^T += K^T dS^T comes from the K tile by
 // transposed reads.
-template <int HG, int BN>
+template <int D, int HG, int BN>
 __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdParams pr) {
   static_assert(BN == 32, "the direct-load tile mapping assumes 32-key tiles");
+  constexpr int KK = D / 16;    // 16-wide reduction steps over d
+  constexpr int DB = D / 32;    // 32-row blocks of dQ^T
+  constexpr int KC = D / 8;     // 16-byte chunks per tile row
+  constexpr int RPP = 64 / KC;  // tile rows per 1 KiB wave-load
+  constexpr int PPW = BN / RPP / 4;  // wave-loads per wave, tensor and tile
   constexpr int QROWS = 32 * (4 / HG);
   constexpr int KB = BN / 32;
   // one array per pipeline slot: the wait-count pass then sees that loads
@@ -461,11 +475,11 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
   const int wkmin = row_keys(pr.m, min(wq0, s_q - 1)).lo;
   const int wkmax = row_keys(pr.m, min(wq0 + 31, s_q - 1)).hi;
 
-  bf16x8 qreg[8], doreg[8];
+  bf16x8 qreg[KK], doreg[KK];
   {
     const int64_t off = ((int64_t)qc * pr.hq + head) * D + hl * 8;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
       qreg[kk] = *reinterpret_cast<const bf16x8*>(pr.q + off + kk * 16);
       doreg[kk] = *reinterpret_cast<const bf16x8*>(pr.dout + off + kk * 16);
     }
@@ -475,15 +489,15 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
   // retire the stationary loads before the loop (see the dK/dV kernel)
   __builtin_amdgcn_s_waitcnt(0);
 
-  f32x16 dqa[4];
+  f32x16 dqa[DB];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) dqa[b] = f32x16{};
+  for (int b = 0; b < DB; ++b) dqa[b] = f32x16{};
 
   const int tstart = (kmin / BN) * BN;
   const int nt = kmax >= kmin ? (kmax - tstart) / BN + 1 : 0;
 
-  // 16 wave-loads of 1 KiB per tile, 4 per wave: wave w brings K and V parts
-  // 2w, 2w+1 (4 keys each), as inline-asm direct loads (see lds_dma16): a
+  // A part is one 1 KiB wave-load (RPP keys of K or V); wave w brings K and V
+  // parts PPW w .. +PPW-1 as inline-asm direct loads (see lds_dma16): a
   // wave-uniform base plus a 32-bit lane offset.
   const int wu = __builtin_amdgcn_readfirstlane(w);  // LDS destinations go to M0
   const uint32_t key_bytes = (uint32_t)pr.hkv * D * 2;
@@ -492,26 +506,27 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
     const uint32_t dv = lds_addr(buf ? &lv1[0] : &lv0[0]);
     const char* kb = reinterpret_cast<const char*>(pr.k) + (int64_t)kvh * (D * 2);
     const char* vb = reinterpret_cast<const char*>(pr.v) + (int64_t)kvh * (D * 2);
-    const uint32_t q = lane >> 4;
+    const int q = lane / KC;  // key within the part; lane % KC is the LDS slot
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int part = 2 * wu + j;
+    for (int j = 0; j < PPW; ++j) {
+      const int part = PPW * wu + j;
       // keys past the end read the last key (always masked)
-      const int first = min(t0 + 4 * part, s_k - 1);
-      const uint32_t rel = (uint32_t)(min(t0 + 4 * part + (int)q, s_k - 1) - first);
-      const uint32_t off = rel * key_bytes + ((uint32_t)((lane & 15) ^ (4 * q + (part & 3))) << 4);
+      const int first = min(t0 + RPP * part, s_k - 1);
+      const uint32_t rel = (uint32_t)(min(t0 + RPP * part + q, s_k - 1) - first);
+      const uint32_t off =
+          rel * key_bytes + ((uint32_t)((lane % KC) ^ swz_row<D>(RPP * part + q)) << 4);
       lds_dma16(kb + (int64_t)first * key_bytes, off, dk + part * 1024);
       lds_dma16(vb + (int64_t)first * key_bytes, off, dv + part * 1024);
     }
   };
   // fragment read offsets (elements) within a tile
-  int kro[8], troff[4][2];
+  int kro[KK], troff[DB][2];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) kro[kk] = ln * D + (((hl + 2 * kk) ^ swz16(ln)) << 3);
+  for (int kk = 0; kk < KK; ++kk) kro[kk] = ln * D + (((hl + 2 * kk) ^ swz_row<D>(ln)) << 3);
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int b = 0; b < DB; ++b)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) troff[b][h] = tr_offset(lane, b, h);
+    for (int h = 0; h < 2; ++h) troff[b][h] = tr_offset<D>(lane, b, h);
 
   if (nt > 0) load_tile(tstart, 0);
   wait_lds_dma();
@@ -531,36 +546,36 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
         // the A fragments of each chain are requested before the chain runs
         const __bf16* kp = (buf ? &lk1[0] : &lk0[0]) + kb * 32 * D;
         const __bf16* vp = (buf ? &lv1[0] : &lv0[0]) + kb * 32 * D;
-        bf16x8 afk[8], afv[8];
+        bf16x8 afk[KK], afv[KK];
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) afk[kk] = *reinterpret_cast<const bf16x8*>(kp + kro[kk]);
+        for (int kk = 0; kk < KK; ++kk) afk[kk] = *reinterpret_cast<const bf16x8*>(kp + kro[kk]);
         sa[kb] = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) sa[kb] = mfma32(afk[kk], qreg[kk], sa[kb]);
+        for (int kk = 0; kk < KK; ++kk) sa[kb] = mfma32(afk[kk], qreg[kk], sa[kb]);
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) afv[kk] = *reinterpret_cast<const bf16x8*>(vp + kro[kk]);
+        for (int kk = 0; kk < KK; ++kk) afv[kk] = *reinterpret_cast<const bf16x8*>(vp + kro[kk]);
         pa[kb] = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) pa[kb] = mfma32(afv[kk], doreg[kk], pa[kb]);
-        // Order: the 8 K fragments, then the S chain with one V fragment read
+        for (int kk = 0; kk < KK; ++kk) pa[kb] = mfma32(afv[kk], doreg[kk], pa[kb]);
+        // Order: the K fragments, then the S chain with one V fragment read
         // after each of its MFMAs (the V reads overlap the chain instead of
         // starting after it), then the dP chain.
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // 8 LDS reads (K)
+        __builtin_amdgcn_sched_group_barrier(0x100, KK, 0);  // LDS reads (K)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < KK; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA (S)
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read (V)
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // the dP chain
+        __builtin_amdgcn_sched_group_barrier(0x008, KK, 0);  // the dP chain
       }
       const bool full = t0 >= free_lo && t0 + BN - 1 <= free_hi;
       // K^T fragments for dQ^T += K^T dS^T, requested before the softmax so
       // that its vector work covers their latency
-      bf16x8 kft[4][2 * KB];
+      bf16x8 kft[DB][2 * KB];
       {
         const __bf16* kt = buf ? &lk1[0] : &lk0[0];
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < DB; ++b)
 #pragma unroll
           for (int ch = 0; ch < 2 * KB; ++ch)
             kft[b][ch] = frag_tr(kt + ch * 16 * D, troff[b][0], troff[b][1]);
@@ -598,7 +613,7 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
 #pragma unroll
       for (int ch = 0; ch < 2 * KB; ++ch)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) dqa[b] = mfma32(kft[b][ch], dst[ch], dqa[b]);
+        for (int b = 0; b < DB; ++b) dqa[b] = mfma32(kft[b][ch], dst[ch], dqa[b]);
     }
     wait_lds_dma();  // the next tile has landed
     __syncthreads();
@@ -609,7 +624,7 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
   }
 
   if (row_ok)
-    store_rows(pr.dq, ((int64_t)qi * pr.hq + head) * D + hl * 4, dqa, pr.scale, pr.grad_f32,
+    store_rows<DB>(pr.dq, ((int64_t)qi * pr.hq + head) * D + hl * 4, dqa, pr.scale, pr.grad_f32,
                pr.accum);
 }
 
@@ -617,15 +632,41 @@ constexpr int kDqKeys = DQ_KEYS;     // keys per dQ tile
 constexpr int kDkdvRows = DKDV_ROWS;      // query rows per dK/dV tile
 constexpr int kDkdvGroups = DKDV_GROUPS;  // 32-key groups (wave pairs) per dK/dV workgroup
 
-template <int HG>
+template <int D, int HG>
 int launch_dq(const BwdParams& p, int g, hipStream_t stream) {
   constexpr int QROWS = 32 * (4 / HG);
   BwdParams pr = p;
   pr.n_blocks = (p.m.s_q + QROWS - 1) / QROWS;
   dim3 grid((unsigned)pr.n_blocks, (unsigned)(p.hkv * (g / HG)));
   TraceScope ts("attn_bwd_dq_bf16", stream);
-  hipLaunchKernelGGL((bwd_dq_kernel<HG, kDqKeys>), grid, dim3(256), 0, stream, pr);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, HG, kDqKeys>), grid, dim3(256), 0, stream, pr);
   return hipGetLastError() == hipSuccess ? USP_OK : USP_ERR_HIP;
+}
+
+// D and LSE * log2(e), then dK/dV, then dQ, for head dim D
+template <int D>
+int bwd_launch(const BwdParams& p, const AttnArgs& a, float* dd, float* lse2) {
+  {
+    const int64_t n = a.s_q * a.hq * (D / 8);
+    TraceScope ts("attn_bwd_rowdot_bf16", a.stream);
+    hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       a.stream, static_cast<const __bf16*>(a.o),
+                       static_cast<const __bf16*>(a.dout), a.lse, dd, lse2, (int)a.s_q, a.hq,
+                       p.s_tq);
+    if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
+  }
+  {
+    constexpr int keys = 32 * kDkdvGroups;
+    dim3 grid((unsigned)((a.s_k + keys - 1) / keys), (unsigned)a.hkv);
+    TraceScope ts("attn_bwd_dkdv_bf16", a.stream);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kDkdvRows, kDkdvGroups>), grid,
+                       dim3(128 * kDkdvGroups), 0, a.stream, p);
+    if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
+  }
+  const int g = a.hq / a.hkv;
+  if (g % 4 == 0) return launch_dq<D, 4>(p, g, a.stream);
+  if (g % 2 == 0) return launch_dq<D, 2>(p, g, a.stream);
+  return launch_dq<D, 1>(p, g, a.stream);
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -644,14 +685,6 @@ int attn_bwd_bf16(const AttnArgs& a) {
   char* ws = static_cast<char*>(a.workspace);
   float* dd = reinterpret_cast<float*>(ws);
   float* lse2 = reinterpret_cast<float*>(ws + align256((size_t)a.hq * s_tq * 4));
-  {
-    const int64_t n = a.s_q * a.hq * 16;
-    TraceScope ts("attn_bwd_rowdot_bf16", a.stream);
-    hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, a.stream,
-                       static_cast<const __bf16*>(a.o), static_cast<const __bf16*>(a.dout), a.lse,
-                       dd, lse2, (int)a.s_q, a.hq, s_tq);
-    if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
-  }
   BwdParams p{};
   p.q = static_cast<const __bf16*>(a.q);
   p.k = static_cast<const __bf16*>(a.k);
@@ -671,18 +704,7 @@ int attn_bwd_bf16(const AttnArgs& a) {
   p.accum = a.accumulate;
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
-  {
-    constexpr int keys = 32 * kDkdvGroups;
-    dim3 grid((unsigned)((a.s_k + keys - 1) / keys), (unsigned)a.hkv);
-    TraceScope ts("attn_bwd_dkdv_bf16", a.stream);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<kDkdvRows, kDkdvGroups>), grid, dim3(128 * kDkdvGroups), 0,
-                       a.stream, p);
-    if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
-  }
-  const int g = a.hq / a.hkv;
-  if (g % 4 == 0) return launch_dq<4>(p, g, a.stream);
-  if (g % 2 == 0) return launch_dq<2>(p, g, a.stream);
-  return launch_dq<1>(p, g, a.stream);
+  return a.d == 64 ? bwd_launch<64>(p, a, dd, lse2) : bwd_launch<128>(p, a, dd, lse2);
 }
 
 }  // namespace usp

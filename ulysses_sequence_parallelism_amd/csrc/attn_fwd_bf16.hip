@@ -1,4 +1,4 @@
-// Attention forward, bf16 in / fp32 accumulate, d = 128, gfx950 matrix cores.
+// Attention forward, bf16 in / fp32 accumulate, d = 128 or 64, gfx950 matrix cores.
 //
 // One rank's share of Ulysses attention is exact softmax attention over the
 // whole sequence for hq query heads sharing hkv key/value heads ("feat(dspark):
@@ -30,15 +30,15 @@
 //   * The probabilities go straight from the accumulator into the B operand of
 //     O^T += V^T P^T (no LDS round trip); V is staged from a key-major copy
 //     whose 16-key chunks are reordered to match (see kmajor.hip).
-//   * Q stays in registers for the whole key loop (8 x 16 bytes per lane).
+//   * Q stays in registers for the whole key loop (d / 16 x 16 bytes per lane).
 //   * K and V^T tiles of 64 keys are double-buffered in LDS and go straight
 //     from global memory into LDS (global_load_lds_dwordx4: no staging
 //     registers, no LDS stores). That load writes each lane's 16 bytes at
 //     consecutive LDS addresses, so rows are unpadded and their 16-byte chunks
-//     XOR-swizzled (chunk c of a 256-byte K row r in slot c ^ (r & 15), of a
-//     128-byte V^T row r in slot c ^ ((r >> 1) & 7)): 16 lanes reading one
-//     chunk of 16 rows hit 16 distinct bank groups. The next tiles' loads are
-//     issued at the start of a step; one barrier per tile.
+//     XOR-swizzled (chunk c of a K row r in slot c ^ swz_row(r), of a 128-byte
+//     V^T row r in slot c ^ ((r >> 1) & 7)): 16 lanes reading one chunk of 16
+//     rows hit 16 distinct bank groups. The next tiles' loads are issued at
+//     the start of a step; one barrier per tile.
 //   * Software pipeline inside each wave: the scores of tile t+1 (MFMA) are
 //     computed in the same straight-line block as the softmax of tile t
 //     (VALU), so the two interleave; boundary tiles and running-max updates
@@ -62,7 +62,6 @@ namespace usp {
 
 namespace {
 
-constexpr int D = 128;
 constexpr int BN = 64;        // keys per tile
 constexpr float kRescaleThreshold = 8.0f;
 
@@ -79,8 +78,14 @@ struct FwdParams {
   float scale_log2;   // softmax scale * log2(e)
 };
 
-template <int HG>
+template <int D, int HG>
 __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
+  constexpr int KK = D / 16;     // 16-wide reduction steps of Q K^T
+  constexpr int DB = D / 32;     // 32-row blocks of O^T
+  constexpr int KC = D / 8;      // 16-byte chunks per K row
+  constexpr int RPP = 64 / KC;   // K rows per 1 KiB wave-load
+  constexpr int KPW = BN / RPP / 8;  // K wave-loads per wave and tile
+  constexpr int VPW = D / 8 / 8;     // V^T wave-loads (8 d-rows each) per wave and tile
   constexpr int QBW = 8 / HG;
   constexpr int QROWS = 32 * QBW;
   // one array per slot: the wait-count pass cannot tell two slots of one
@@ -123,20 +128,20 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
   const int wkmax = row_keys(pr.m, min(wq0 + 31, s_q - 1)).hi;
 
   // Q fragment: B operand of S^T = K Q^T, lane holds Q[qc][16kk + 8hl .. +7]
-  bf16x8 qreg[8];
+  bf16x8 qreg[KK];
   {
     const __bf16* qp = pr.q + ((int64_t)qc * pr.hq + head) * D + hl * 8;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
+    for (int kk = 0; kk < KK; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
   }
   // Retire the Q loads here; otherwise the wait-count pass treats them as
   // possibly in flight inside the loop and makes the MFMAs wait for the next
   // tile's loads too.
   __builtin_amdgcn_s_waitcnt(0);
 
-  f32x16 oacc[4];
+  f32x16 oacc[DB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
   const int tstart = (kmin / BN) * BN;
@@ -147,9 +152,9 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
   // and can interleave. K runs one tile ahead of V: at the start of step t,
   // K(t+2) goes into K(t)'s slot and V(t+1) into V(t-1)'s (both last read in
   // step t-1), so each needs two slots and there is one barrier per tile.
-  // Wave w loads K parts 2w, 2w+1 (4 keys each) and V^T parts 2w, 2w+1 (8
-  // d-rows each) as inline-asm direct loads (lds_dma16): a wave-uniform base
-  // plus a 32-bit lane offset.
+  // A part is one 1 KiB wave-load: RPP keys of K or 8 d-rows of V^T. Wave w
+  // loads K parts KPW w .. +KPW-1 and V^T parts VPW w .. +VPW-1 as inline-asm
+  // direct loads (lds_dma16): a wave-uniform base plus a 32-bit lane offset.
   const int wu = __builtin_amdgcn_readfirstlane(w);  // LDS destinations go to M0
   const uint32_t key_bytes = (uint32_t)pr.hkv * D * 2;
   const uint32_t vt_row_bytes = (uint32_t)pr.s_t * 2;
@@ -157,14 +162,15 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
     const int t0 = tstart + t * BN;
     const uint32_t dst = lds_addr(kslot(slot));
     const char* kb = reinterpret_cast<const char*>(pr.k) + (int64_t)kvh * (D * 2);
-    const uint32_t q = lane >> 4;
+    const int q = lane / KC;  // key within the part; lane % KC is the LDS slot
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int part = 2 * wu + j;
+    for (int j = 0; j < KPW; ++j) {
+      const int part = KPW * wu + j;
       // keys past the end read the last key (always masked)
-      const int first = min(t0 + 4 * part, s_k - 1);
-      const uint32_t rel = (uint32_t)(min(t0 + 4 * part + (int)q, s_k - 1) - first);
-      const uint32_t off = rel * key_bytes + ((uint32_t)((lane & 15) ^ (4 * (part & 3) + q)) << 4);
+      const int first = min(t0 + RPP * part, s_k - 1);
+      const uint32_t rel = (uint32_t)(min(t0 + RPP * part + q, s_k - 1) - first);
+      const uint32_t off =
+          rel * key_bytes + ((uint32_t)((lane % KC) ^ swz_row<D>(RPP * part + q)) << 4);
       lds_dma16(kb + (int64_t)first * key_bytes, off, dst + part * 1024);
     }
   };
@@ -172,18 +178,19 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
     const int t0 = tstart + t * BN;
     const uint32_t dst = lds_addr(vslot(slot));
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int part = 2 * wu + j;
+    for (int j = 0; j < VPW; ++j) {
+      const int part = VPW * wu + j;
       const char* b = reinterpret_cast<const char*>(pr.vt + ((int64_t)kvh * D + 8 * part) * pr.s_t + t0);
+      // row 8 part + lane / 8 sits in slot chunk ^ ((row >> 1) & 7)
       const uint32_t off = (uint32_t)(lane >> 3) * vt_row_bytes +
-                           ((uint32_t)((lane & 7) ^ (4 * j + (lane >> 4))) << 4);
+                           ((uint32_t)((lane & 7) ^ (4 * (part & 1) + (lane >> 4))) << 4);
       lds_dma16(b, off, dst + part * 1024);
     }
   };
   // fragment read offsets (elements) within a tile
-  int kro[8], vro[4];
+  int kro[KK], vro[4];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) kro[kk] = ln * D + (((hl + 2 * kk) ^ (ln & 15)) << 3);
+  for (int kk = 0; kk < KK; ++kk) kro[kk] = ln * D + (((hl + 2 * kk) ^ swz_row<D>(ln)) << 3);
 #pragma unroll
   for (int ch = 0; ch < 4; ++ch) vro[ch] = ln * BN + (((hl + 2 * ch) ^ ((ln >> 1) & 7)) << 3);
   // S^T = K Q^T for the two 32-key blocks of the tile in slot buf
@@ -191,7 +198,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const __bf16* kp = kslot(buf) + kb * 32 * D;
@@ -242,7 +249,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
           const float mnew = need ? mx : m_run;
           const float alpha = need ? exp2f(m_run - mnew) : 1.f;
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
+          for (int b = 0; b < DB; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
           l_run *= alpha;
@@ -280,7 +287,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
 #pragma unroll
       for (int ch = 0; ch < 4; ++ch) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < DB; ++b) {
           const __bf16* vp = vslot(buf) + b * 32 * BN;
           oacc[b] = mfma32(*reinterpret_cast<const bf16x8*>(vp + vro[ch]), pb[ch], oacc[b]);
         }
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
       // shadows.
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
+      for (int i = 0; i < 2 * KK + 4 * DB; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
       }
@@ -310,7 +317,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
     const int64_t ob = ((int64_t)qi * pr.hq + head) * D + hl * 4;
     if (pr.o32 != nullptr) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < DB; ++b)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           f32x4 v4 = {oacc[b][4 * r] * inv, oacc[b][4 * r + 1] * inv, oacc[b][4 * r + 2] * inv,
@@ -319,7 +326,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
         }
     } else {
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < DB; ++b)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           u32x2 v2 = {pack_bf16x2(oacc[b][4 * r] * inv, oacc[b][4 * r + 1] * inv),
@@ -332,15 +339,22 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
   }
 }
 
-template <int HG>
+template <int D, int HG>
 int launch_fwd(const FwdParams& p, int g, int hkv, hipStream_t stream) {
   constexpr int QROWS = 32 * (8 / HG);
   FwdParams pr = p;
   pr.n_qblocks = (p.m.s_q + QROWS - 1) / QROWS;
   dim3 grid((unsigned)pr.n_qblocks, (unsigned)(hkv * (g / HG)));
   TraceScope ts("attn_fwd_bf16", stream);
-  hipLaunchKernelGGL((fwd_bf16_kernel<HG>), grid, dim3(512), 0, stream, pr);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, HG>), grid, dim3(512), 0, stream, pr);
   return hipGetLastError() == hipSuccess ? USP_OK : USP_ERR_HIP;
+}
+
+template <int D>
+int fwd_dispatch(const FwdParams& p, int g, int hkv, hipStream_t stream) {
+  if (g % 4 == 0) return launch_fwd<D, 4>(p, g, hkv, stream);
+  if (g % 2 == 0) return launch_fwd<D, 2>(p, g, hkv, stream);
+  return launch_fwd<D, 1>(p, g, hkv, stream);
 }
 
 }  // namespace
@@ -351,7 +365,7 @@ size_t attn_fwd_bf16_workspace(int64_t s_k, int, int hkv, int d) {
 
 int attn_fwd_bf16(const AttnArgs& a) {
   const int64_t s_t = kmajor_len(a.s_k);
-  int rc = kmajor_launch(a.v, a.workspace, a.s_k, a.hkv, s_t, a.stream, "attn_fwd_kmajor_v");
+  int rc = kmajor_launch(a.v, a.workspace, a.s_k, a.hkv, a.d, s_t, a.stream, "attn_fwd_kmajor_v");
   if (rc != USP_OK) return rc;
   FwdParams p{};
   p.q = static_cast<const __bf16*>(a.q);
@@ -366,9 +380,7 @@ int attn_fwd_bf16(const AttnArgs& a) {
   p.hkv = a.hkv;
   p.scale_log2 = a.scale * kLog2e;
   const int g = a.hq / a.hkv;
-  if (g % 4 == 0) return launch_fwd<4>(p, g, a.hkv, a.stream);
-  if (g % 2 == 0) return launch_fwd<2>(p, g, a.hkv, a.stream);
-  return launch_fwd<1>(p, g, a.hkv, a.stream);
+  return a.d == 64 ? fwd_dispatch<64>(p, g, a.hkv, a.stream) : fwd_dispatch<128>(p, g, a.hkv, a.stream);
 }
 
 }  // namespace usp

@@ -49,8 +49,7 @@ int check_heads(int hq, int hkv, int d, float scale, int causal, int dtype) {
   if (hq < 1 || hkv < 1 || hq % hkv != 0) return USP_ERR_INVALID;
   if (!(scale > 0.f) || !isfinite(scale)) return USP_ERR_INVALID;
   if (causal != 0 && causal != 1) return USP_ERR_INVALID;
-  if (dtype == USP_BF16 && d != 128) return USP_ERR_UNSUPPORTED;
-  if (dtype == USP_FP32 && d != 64 && d != 128) return USP_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return USP_ERR_UNSUPPORTED;
   return USP_OK;
 }
 

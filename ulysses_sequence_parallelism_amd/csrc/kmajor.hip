@@ -1,4 +1,5 @@
-// Key-major (transposed) copies of a [s_pad][H][128] bf16 tensor for gfx950.
+// Key-major (transposed) copies of a [s_pad][H][d] bf16 tensor (d = 128 or 64)
+// for gfx950.
 //
 // In the attention kernels the matrix-core reduction axis of P.V (forward),
 // of dS.K (dQ) and of P^T.dO, dS^T.Q (dK/dV) is the sequence axis. A 32x32x16
@@ -10,9 +11,9 @@
 // accumulator, so both operands are read with single 16-byte loads.
 // Slots at and beyond s_pad are written as zero.
 //
-// One block transposes a 64-position x 128-column tile of one head through
-// LDS: 16-byte coalesced loads from the row-major tensor, then every lane
-// gathers 8 positions of one column and writes one 16-byte chunk.
+// One block transposes a 64-position x d-column tile of one head through LDS:
+// 16-byte coalesced loads from the row-major tensor, then every lane gathers 8
+// positions of one column and writes one 16-byte chunk.
 #include "usp_common.h"
 #include "usp_internal.h"
 
@@ -20,21 +21,22 @@ namespace usp {
 
 namespace {
 
-constexpr int D = 128;
 constexpr int T = 64;
-constexpr int P = D + 8;  // LDS row pitch (elements)
 
+template <int D>
 __global__ __launch_bounds__(256) void kmajor_kernel(const unsigned short* __restrict__ src,
                                                      unsigned short* __restrict__ dst,
                                                      int s_pad, int heads, int64_t s_t) {
+  constexpr int P = D + 8;   // LDS row pitch (elements)
+  constexpr int KC = D / 8;  // 16-byte chunks per row
   __shared__ __attribute__((aligned(16))) unsigned short tile[T * P];
   const int h = blockIdx.y;
   const int s0 = blockIdx.x * T;
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < T * KC / 256; ++u) {
     const int e = tid + 256 * u;
-    const int r = e >> 4, c = e & 15;
+    const int r = e / KC, c = e % KC;
     const int s = s0 + r;
     u32x4 val = {0u, 0u, 0u, 0u};
     if (s < s_pad) val = *reinterpret_cast<const u32x4*>(src + ((int64_t)s * heads + h) * D + c * 8);
@@ -42,7 +44,7 @@ __global__ __launch_bounds__(256) void kmajor_kernel(const unsigned short* __res
   }
   __syncthreads();
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < D * (T / 8) / 256; ++u) {
     const int e = tid + 256 * u;
     const int col = e >> 3, c8 = e & 7;  // output row (column of src), 8-slot chunk
     unsigned w[4];
@@ -60,13 +62,16 @@ __global__ __launch_bounds__(256) void kmajor_kernel(const unsigned short* __res
 
 }  // namespace
 
-int kmajor_launch(const void* src, void* dst, int64_t s_pad, int heads, int64_t s_t,
+int kmajor_launch(const void* src, void* dst, int64_t s_pad, int heads, int d, int64_t s_t,
                   hipStream_t stream, const char* trace_name) {
   dim3 grid((unsigned)(s_t / T), (unsigned)heads);
   TraceScope ts(trace_name, stream);
-  hipLaunchKernelGGL(kmajor_kernel, grid, dim3(256), 0, stream,
-                     static_cast<const unsigned short*>(src), static_cast<unsigned short*>(dst),
-                     (int)s_pad, heads, s_t);
+  auto* s = static_cast<const unsigned short*>(src);
+  auto* o = static_cast<unsigned short*>(dst);
+  if (d == 64)
+    hipLaunchKernelGGL(kmajor_kernel<64>, grid, dim3(256), 0, stream, s, o, (int)s_pad, heads, s_t);
+  else
+    hipLaunchKernelGGL(kmajor_kernel<128>, grid, dim3(256), 0, stream, s, o, (int)s_pad, heads, s_t);
   return hipGetLastError() == hipSuccess ? USP_OK : USP_ERR_HIP;
 }
 

@@ -43,6 +43,22 @@ __host__ __device__ __forceinline__ int kperm(int p) {
 // (row-major fragment reads) and 4 consecutive chunks of 4 consecutive rows
 // starting at a multiple of 4 (transposed reads).
 __host__ __device__ __forceinline__ int swz16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// The same for 128-byte rows (8 chunks; two rows share a 256-byte bank line,
+// row r in half r & 1): c ^ swz8(r) with swz8 = (r1, r3, r2) from row bits
+// r1..r3. For one row parity it is a bijection of r >> 1, so one chunk of 16
+// consecutive rows hits 16 distinct slots; rows 4m + e and 4m + e + 2 differ in
+// bit 2, so 4 consecutive chunks (4-aligned) of 4 consecutive rows (4-aligned)
+// fill the two halves of both bank lines.
+__host__ __device__ __forceinline__ int swz8(int r) {
+  return (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1);
+}
+// Chunk swizzle of a tile with D-element bf16 rows (D = 128 or 64).
+template <int D>
+__host__ __device__ __forceinline__ int swz_row(int r) {
+  static_assert(D == 128 || D == 64, "head dim 64 or 128");
+  if constexpr (D == 128) return swz16(r);
+  else return swz8(r);
+}
 
 // Transposed LDS read (ds_read_b64_tr_b16). Lanes act in groups of 16: each
 // names 4 consecutive bf16 values, and lane i of a group receives value i%4
@@ -54,16 +70,17 @@ __device__ __forceinline__ bf16x4_v lds_read_tr(const __bf16* p) {
       (__attribute__((address_space(3))) bf16x4_v*)(const_cast<__bf16*>(p)));
 }
 
-// Element offset, in a tile of 128-element rows stored with swz16, that lane
-// `lane` names in transposed read h (0 or 1) of column block b, for the
+// Element offset, in a tile of D-element rows stored with swz_row<D>, that
+// lane `lane` names in transposed read h (0 or 1) of column block b, for the
 // 16-row chunk at row 0. Reads h = 0 and h = 1 together give the lane column
 // 32b + lane%32 of rows 8h + 4(lane/32) + j, j = 0..3: the 32x32x16 operand
 // (m = column, k = row) in the k-order in which the other operand leaves a
 // 32x32 accumulator (see kperm).
+template <int D>
 __device__ __forceinline__ int tr_offset(int lane, int b, int h) {
   const int r = 8 * h + 4 * (lane >> 5) + ((lane >> 2) & 3);
   const int c = 4 * b + 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
-  return r * 128 + ((c ^ swz16(r)) << 3) + 4 * (lane & 1);
+  return r * D + ((c ^ swz_row<D>(r)) << 3) + 4 * (lane & 1);
 }
 __device__ __forceinline__ bf16x8 frag_tr(const __bf16* tile, int off0, int off1) {
   const bf16x4_v a = lds_read_tr(tile + off0), b = lds_read_tr(tile + off1);

@@ -100,7 +100,9 @@ inline MaskGeom mask_geom(const AttnArgs& a) {
   return m;
 }
 
-int kmajor_launch(const void* src, void* dst, int64_t s_pad, int heads, int64_t s_t,
+// Key-major copy of a [s_pad][heads][d] bf16 tensor (d = 128 or 64) into
+// [heads][d][s_t], reordered within 16-position chunks (kmajor.hip).
+int kmajor_launch(const void* src, void* dst, int64_t s_pad, int heads, int d, int64_t s_t,
                   hipStream_t stream, const char* trace_name);
 
 size_t attn_fwd_bf16_workspace(int64_t s_k, int hq, int hkv, int d);
