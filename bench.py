@@ -436,27 +436,44 @@ def main():
                 "avg_launch_ms": round(dom_avg_ms, 4),
                 "algorithmic_flop_per_launch": dom_flops}
 
-    # ---- composite permute bandwidth (all P ranks' Q, K, V; not part of the step)
-    ys = {t: torch.empty((p, s_pad, full[t].shape[1] // p, d), dtype=torch.bfloat16, device=dev)
-          for t in (workloads.Q, workloads.K, workloads.V)}
-    nbytes = sum(full[t].numel() * 2 + ys[t].numel() * 2 for t in ys)
-
-    def pack_all():
-        for t in ys:
-            usp.usp_pad_pack_seq2head(full[t], p, out=ys[t])
-
-    for _ in range(3):
-        pack_all()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # ---- composite permute bandwidth (all P ranks' Q, K, V; not part of the step).
+    # Passes rotate over n_sets buffer sets with n_sets * bytes >= 1 GiB, four
+    # times the 256 MB last-level (MALL) cache, so no pass finds its data there.
+    pk = (workloads.Q, workloads.K, workloads.V)
+    nbytes = int(sum(full[t].numel() * 2 + p * s_pad * (full[t].shape[1] // p) * d * 2 for t in pk))
+    n_sets = max(1, -(-(1 << 30) // nbytes))
+    srcs = [full] + [{t: full[t].clone() for t in pk} for _ in range(n_sets - 1)]
+    ys = [{t: torch.empty((p, s_pad, full[t].shape[1] // p, d), dtype=torch.bfloat16, device=dev)
+           for t in pk} for _ in range(n_sets)]
     reps = 20
-    e0.record()
-    for _ in range(reps):
-        pack_all()
-    e1.record()
-    torch.cuda.synchronize()
-    pack_ms = e0.elapsed_time(e1) / reps
+
+    def timed(fn):
+        for i in range(3):
+            fn(i % n_sets)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(i % n_sets)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def pack_all(i):
+        for t in pk:
+            usp.usp_pad_pack_seq2head(srcs[i][t], p, out=ys[i][t])
+
+    pack_ms = timed(pack_all)
     permute_gbs = nbytes / (pack_ms * 1e-3) / 1e9
+    # reference copy on the same box: torch's device-to-device copy (the
+    # runtime's blit kernel) reading and writing the same total number of
+    # bytes, rotated the same way
+    del srcs, ys
+    cin = [torch.empty(nbytes // 2, dtype=torch.uint8, device=dev).fill_(1) for _ in range(n_sets)]
+    cout = [torch.empty_like(x) for x in cin]
+    copy_ms = timed(lambda i: cout[i].copy_(cin[i]))
+    copy_gbs = 2 * (nbytes // 2) / (copy_ms * 1e-3) / 1e9
+    del cin, cout
 
     out = {
         "metric": METRIC,
@@ -489,6 +506,9 @@ def main():
         "permute_gbps": round(permute_gbs, 1),
         "permute_frac_of_hbm_peak": round(permute_gbs / PEAK_HBM_GBS, 4),
         "permute_bytes": nbytes,
+        "permute_buffer_sets": n_sets,
+        "d2d_memcpy_gbps": round(copy_gbs, 1),
+        "permute_over_d2d_memcpy": round(permute_gbs / copy_gbs, 4),
         "kernels_ms_per_step": {e["name"]: round(e["total_ms"] / args.steps, 4) for e in trace},
         "wall_s_timed": round(t_wall, 3),
         "roofline": roofline,
