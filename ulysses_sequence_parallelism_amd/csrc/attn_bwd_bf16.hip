@@ -38,16 +38,6 @@
 #include "usp_common.h"
 #include "usp_internal.h"
 
-#ifndef DQ_KEYS
-#define DQ_KEYS 32
-#endif
-#ifndef DKDV_ROWS
-#define DKDV_ROWS 64
-#endif
-#ifndef DKDV_GROUPS
-#define DKDV_GROUPS 4
-#endif
-
 namespace usp {
 
 namespace {
@@ -628,9 +618,9 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
                pr.accum);
 }
 
-constexpr int kDqKeys = DQ_KEYS;     // keys per dQ tile
-constexpr int kDkdvRows = DKDV_ROWS;      // query rows per dK/dV tile
-constexpr int kDkdvGroups = DKDV_GROUPS;  // 32-key groups (wave pairs) per dK/dV workgroup
+constexpr int kDqKeys = 32;      // keys per dQ tile
+constexpr int kDkdvRows = 64;    // query rows per dK/dV tile
+constexpr int kDkdvGroups = 4;   // 32-key groups (wave pairs) per dK/dV workgroup
 
 template <int D, int HG>
 int launch_dq(const BwdParams& p, int g, hipStream_t stream) {
