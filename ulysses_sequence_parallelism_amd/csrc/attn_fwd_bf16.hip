@@ -187,12 +187,24 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
       lds_dma16(b, off, dst + part * 1024);
     }
   };
-  // fragment read offsets (elements) within a tile
-  int kro[KK], vro[4];
+  // LDS byte addresses of the lane's fragments in slot 0 of each array, kept
+  // opaque to the compiler: a read of slot s, block b is then one register
+  // plus a constant in the read's 16-bit offset field. With element offsets
+  // the compiler kept more address registers and spilled.
+  uint32_t kra[KK], vra[4];
+  {
+    const uint32_t kb0 = lds_addr(&lk0[0]), vb0 = lds_addr(&lv0[0]);
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) kro[kk] = ln * D + (((hl + 2 * kk) ^ swz_row<D>(ln)) << 3);
+    for (int kk = 0; kk < KK; ++kk) {
+      kra[kk] = kb0 + 2 * (ln * D + (((hl + 2 * kk) ^ swz_row<D>(ln)) << 3));
+      asm volatile("" : "+v"(kra[kk]));
+    }
 #pragma unroll
-  for (int ch = 0; ch < 4; ++ch) vro[ch] = ln * BN + (((hl + 2 * ch) ^ ((ln >> 1) & 7)) << 3);
+    for (int ch = 0; ch < 4; ++ch) {
+      vra[ch] = vb0 + 2 * (ln * BN + (((hl + 2 * ch) ^ ((ln >> 1) & 7)) << 3));
+      asm volatile("" : "+v"(vra[ch]));
+    }
+  }
   // S^T = K Q^T for the two 32-key blocks of the tile in slot buf
   auto scores = [&](int buf, f32x16* sacc) {
     sacc[0] = f32x16{};
@@ -201,8 +213,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
     for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const __bf16* kp = kslot(buf) + kb * 32 * D;
-        sacc[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kp + kro[kk]), qreg[kk], sacc[kb]);
+        const bf16x8 kf = lds_read_b128(kra[kk] + (uint32_t)(buf * BN * D + kb * 32 * D) * 2);
+        sacc[kb] = mfma32(kf, qreg[kk], sacc[kb]);
       }
     }
   };
@@ -218,8 +230,9 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
   if (nt > 0) scores(0, sa);
   __syncthreads();  // S(0) is read from slot 0 before iteration 0 refills it
 
-  // one pipeline step; the score buffers swap roles every step, so the loop
-  // is unrolled by two instead of copying the next scores over the current
+  // one pipeline step; the score buffers and the slots swap roles every step,
+  // so the loop is unrolled instead of copying the next scores over the
+  // current
   auto step = [&](int it, f32x16 (&scur)[2], f32x16 (&snext)[2], auto parity) {
       const int t0 = tstart + it * BN;
       constexpr int buf = decltype(parity)::value;  // == it & 1; K is read from slot buf ^ 1, V from buf
@@ -288,8 +301,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
       for (int ch = 0; ch < 4; ++ch) {
 #pragma unroll
         for (int b = 0; b < DB; ++b) {
-          const __bf16* vp = vslot(buf) + b * 32 * BN;
-          oacc[b] = mfma32(*reinterpret_cast<const bf16x8*>(vp + vro[ch]), pb[ch], oacc[b]);
+          const bf16x8 vf = lds_read_b128(vra[ch] + (uint32_t)(buf * D * BN + b * 32 * BN) * 2);
+          oacc[b] = mfma32(vf, pb[ch], oacc[b]);
         }
       }
       // Instruction order for this block: fragment reads run four ahead of
@@ -306,10 +319,19 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
       wait_lds_dma();  // this step's loads have landed
       __syncthreads();
   };
-  for (int it = 0; it < nt; it += 2) {
+  // Whole groups of four steps in the loop, the remainder after it. A loop
+  // with one exit keeps the softmax state in the same registers throughout;
+  // with an exit after every step this compiler needed about 20 more VGPRs.
+  int it = 0;
+  for (; it + 4 <= nt; it += 4) {
     step(it, sa, sb, std::integral_constant<int, 0>{});
-    if (it + 1 < nt) step(it + 1, sb, sa, std::integral_constant<int, 1>{});
+    step(it + 1, sb, sa, std::integral_constant<int, 1>{});
+    step(it + 2, sa, sb, std::integral_constant<int, 0>{});
+    step(it + 3, sb, sa, std::integral_constant<int, 1>{});
   }
+  if (it < nt) step(it, sa, sb, std::integral_constant<int, 0>{});
+  if (it + 1 < nt) step(it + 1, sb, sa, std::integral_constant<int, 1>{});
+  if (it + 2 < nt) step(it + 2, sa, sb, std::integral_constant<int, 0>{});
 
   const float l_tot = half_swap_sum(l_run);
   if (row_ok) {

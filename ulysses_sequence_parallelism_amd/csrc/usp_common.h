@@ -110,6 +110,11 @@ __device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint3
 }
 #pragma clang diagnostic pop
 __device__ __forceinline__ void wait_lds_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// 16-byte LDS read at byte address a. With a = base + constant, the constant
+// goes into the instruction's 16-bit offset field when it fits.
+__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t a) {
+  return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)a;
+}
 // LDS byte address of a pointer into a __shared__ array, made wave-uniform
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane(
