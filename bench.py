@@ -128,12 +128,17 @@ def cpu_baseline(w, rows: int):
         x = workloads.tensor(w, t, s=r)   # same draw prefix as the full tensor
         share.append(x[:, : heads // p].to(torch.float64).numpy())
     q, k, v, do = share
+    # packed documents: the ones that start inside the prefix, the last cut at r
+    cu = None
+    if w.thd:
+        cu = [c for c in workloads.cu_seqlens(workloads.doc_lengths(w.s)).tolist() if c < r] + [r]
     # the generator draws row-major, so the first r rows equal the full tensor's
     t0 = time.perf_counter()
-    o, lse = oracle.attn_fwd(q, k, v, w.scale)
-    oracle.attn_bwd(q, k, v, o, lse, do, w.scale)
+    o, lse = oracle.attn_fwd(q, k, v, w.scale, r, cu, True)
+    oracle.attn_bwd(q, k, v, o, lse, do, w.scale, r, cu, True)
     dt = time.perf_counter() - t0
-    flops = (4 + 10) * w.d * w.hq * causal_pairs(r)
+    pairs = causal_pairs(r) if cu is None else sum(causal_pairs(b - a) for a, b in zip(cu, cu[1:]))
+    flops = (4 + 10) * w.d * w.hq * pairs
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"causal prefix rows 0..{r - 1} of the {w.name} rank share "
                       f"({w.hq} Q / {w.hkv} KV heads, d={w.d}): fp64 forward + full backward, "
@@ -336,9 +341,14 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     w = workloads.WORKLOADS[args.workload]
-    if w.dtype != "bf16" or w.thd:
-        print("bench workloads: s8k, s32k, s120k, s120k_pad", file=sys.stderr)
+    if w.dtype != "bf16":
+        print("bench workloads: s8k, s32k, s120k, s120k_pad, thd131k", file=sys.stderr)
         sys.exit(2)
+    if w.thd and args.path != "ulysses":
+        print("--path ring / cp / bidir use the unpacked workloads", file=sys.stderr)
+        sys.exit(2)
+    # packed documents (host list: the binding checks it and uploads it)
+    cu = workloads.cu_seqlens(workloads.doc_lengths(w.s)).tolist() if w.thd else None
     p, s_pad, s_loc = w.p, w.s_pad, w.s_pad // w.p
     hq, hkv, d = w.hq, w.hkv, w.d
 
@@ -370,10 +380,11 @@ def main():
     def step():
         for t in (workloads.Q, workloads.K, workloads.V):
             usp.usp_pad_pack_seq2head(local[t], p, out=send[t])
-        usp.usp_attn_fwd(q, k, v, s_valid=w.s, out=o, lse=lse, workspace=ws_f)
+        usp.usp_attn_fwd(q, k, v, s_valid=w.s, cu_seqlens=cu, out=o, lse=lse, workspace=ws_f)
         usp.usp_unpack_head2seq(o.view(p, s_loc, hq, d), s_loc, out=back["o"])
         usp.usp_pad_pack_seq2head(local[workloads.DO], p, out=send[workloads.DO])
-        usp.usp_attn_bwd(q, k, v, o, lse, do, s_valid=w.s, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+        usp.usp_attn_bwd(q, k, v, o, lse, do, s_valid=w.s, cu_seqlens=cu, dq=dq, dk=dk, dv=dv,
+                         workspace=ws_b)
         for n, a in (("dq", dq), ("dk", dk), ("dv", dv)):
             usp.usp_unpack_head2seq(a.view(p, s_loc, a.shape[1], d), s_loc, out=back[n])
 
@@ -413,7 +424,12 @@ def main():
     step_ms = evs[0].elapsed_time(evs[-1]) / args.steps
     per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
 
-    pairs = causal_pairs(w.s_pad) if w.s == w.s_pad else causal_pairs(w.s) + (w.s_pad - w.s) * w.s
+    if cu is not None:
+        pairs = sum(causal_pairs(b - a) for a, b in zip(cu, cu[1:]))
+    elif w.s == w.s_pad:
+        pairs = causal_pairs(w.s_pad)
+    else:
+        pairs = causal_pairs(w.s) + (w.s_pad - w.s) * w.s
     f_fwd = 4 * d * hq * pairs
     f_bwd = 10 * d * hq * pairs
     per = {e["name"]: e for e in trace}
@@ -476,7 +492,8 @@ def main():
     del cin, cout
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if w.name == "s120k" else
+                  f"attn TFLOP/s fwd & fwd+bwd, workload {w.name}; permute GB/s",
         "value": round((f_fwd + f_bwd) / (step_ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -492,7 +509,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: one Ulysses rank's attention layer, S={w.s} "
                                f"(s_pad {w.s_pad}), SP degree {p}, {hq} Q / {hkv} KV heads, "
-                               f"d={d}, causal, forward+backward, pack/unpack of the rank's slice",
+                               f"d={d}, causal"
+                               + (f" within {len(cu) - 1} packed documents" if cu else "")
+                               + ", forward+backward, pack/unpack of the rank's slice",
                    "seq_len": w.s, "sp_degree": p, "heads_q": hq, "heads_kv": hkv,
                    "head_dim": d, "causal": True},
         "attn_fwd_ms": round(fwd_ms, 3),
