@@ -438,7 +438,8 @@ def main():
         return sum(per[n]["total_ms"] for n in names if n in per) / args.steps
 
     fwd_ms = kms("attn_fwd_kmajor_v", "attn_fwd_bf16")
-    bwd_ms = kms("attn_bwd_kmajor", "attn_bwd_rowdot_bf16", "attn_bwd_dkdv_bf16", "attn_bwd_dq_bf16")
+    bwd_ms = kms("attn_bwd_kmajor", "attn_bwd_rowdot_bf16", "attn_bwd_dkdv_bf16",
+                 "attn_bwd_dkdv_reduce", "attn_bwd_dq_bf16")
     perm_ms = kms("pack_seq2head", "unpack_head2seq")
 
     # ---- dominant kernel roofline

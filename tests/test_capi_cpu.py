@@ -223,21 +223,38 @@ def test_merge_argument_errors(L):
     assert merge(L, o=A + (1 << 24)) == INVALID               # O over lse_a
 
 
+def dkdv_chunks(s_q, s_k, hkv):
+    """Row chunks per key block of the bf16 dK/dV kernel: 1 when the 128-key
+    blocks give at least 512 workgroups, else enough for about 1024 (block,
+    chunk) items, at most 16 and at most the number of 64-row tiles."""
+    items = -(-s_k // 128) * hkv
+    if items >= 512:
+        return 1
+    return max(1, min(-(-1024 // items), -(-s_q // 64), 16))
+
+
 def test_workspace_sizes(L):
     for s in (1, 100, 128, 129, 120000, 131072):
         f = L.usp_attn_fwd_workspace_bytes(s, 4, 1, 128, BF16)
         b = L.usp_attn_bwd_workspace_bytes(s, 4, 1, 128, BF16)
         assert f >= 128 * s * 2 and f % 16 == 0
+        # fp32 partial dK and dV per row chunk when the rows are split
+        n = dkdv_chunks(s, s, 1)
+        part = 2 * n * s * 128 * 4 if n > 1 else 0
         # D and LSE * log2(e) per (head, row), fp32
-        assert 2 * 4 * s * 4 <= b < 2 * 4 * (s + 128) * 4 + 512
+        assert 2 * 4 * s * 4 <= b - part < 2 * 4 * (s + 128) * 4 + 512
+    assert dkdv_chunks(120000, 120000, 1) == 1 and dkdv_chunks(8192, 8192, 1) == 16
+    assert dkdv_chunks(32768, 32768, 1) == 4 and dkdv_chunks(100, 100, 1) == 2
     assert L.usp_attn_fwd_workspace_bytes(512, 4, 2, 64, FP32) == 0
     assert L.usp_attn_bwd_workspace_bytes(512, 4, 2, 64, FP32) == 512 * 4 * 4
     assert L.usp_attn_fwd_workspace_bytes(0, 4, 1, 128, BF16) == 0
-    # interval: sized by the query rows only
-    for s_q, s_k in ((100, 1000), (1000, 100), (512, 512)):
-        b = L.usp_attn_bwd_interval_workspace_bytes(s_q, s_k, 4, 1, 128, BF16)
-        assert 2 * 4 * s_q * 4 <= b < 2 * 4 * (s_q + 128) * 4 + 512
-        assert b == L.usp_attn_bwd_interval_workspace_bytes(s_q, 7, 4, 1, 128, BF16)
+    # interval: the query rows and, through the row chunks, the keys
+    for s_q, s_k in ((100, 1000), (1000, 100), (512, 512), (30000, 30000)):
+        for hkv, d in ((1, 128), (4, 64)):
+            b = L.usp_attn_bwd_interval_workspace_bytes(s_q, s_k, 4 * hkv, hkv, d, BF16)
+            n = dkdv_chunks(s_q, s_k, hkv)
+            part = 2 * n * s_k * hkv * d * 4 if n > 1 else 0
+            assert 2 * 4 * hkv * s_q * 4 <= b - part < 2 * 4 * hkv * (s_q + 128) * 4 + 512
     assert L.usp_attn_bwd_interval_workspace_bytes(512, 512, 4, 1, 128, BF16) == \
         L.usp_attn_bwd_workspace_bytes(512, 4, 1, 128, BF16)
     assert L.usp_attn_bwd_interval_workspace_bytes(300, 700, 4, 2, 64, FP32) == 300 * 4 * 4

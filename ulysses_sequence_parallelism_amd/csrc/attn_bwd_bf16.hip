@@ -89,6 +89,11 @@ struct BwdParams {
   MaskGeom m;
   int64_t s_tq;        // row length of lse2 and dd
   int hq, hkv, n_blocks;
+  // dK/dV row chunks: grid x = n_kb key blocks x n_ch chunks of cht row tiles;
+  // with n_ch > 1 each chunk's fp32 partial dV, dK goes to part
+  // ([2][n_ch][s_k][hkv][D], dV first), summed afterwards in chunk order
+  int n_kb, n_ch, cht;
+  float* part;
   int grad_f32, accum;  // fp32 gradients; add to the existing contents
   float scale, scale_log2;
 };
@@ -174,7 +179,10 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
   const int s_q = pr.m.s_q, s_k = pr.m.s_k, s_kv = pr.m.s_kv;
   const int g = pr.hq / pr.hkv;
   const int kvh = blockIdx.y;
-  const int j0 = blockIdx.x * KEYS;
+  // (key block, row chunk) of this workgroup, chunk-major: the workgroups
+  // resident together work on the same rows
+  const int cch = (int)blockIdx.x / pr.n_kb, kbi = (int)blockIdx.x % pr.n_kb;
+  const int j0 = kbi * KEYS;
   const int j1 = min(j0 + KEYS, s_k);
   const int wj0 = j0 + grp * 32;
   const int key = wj0 + ln;
@@ -213,7 +221,12 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
   for (int b = 0; b < DB; ++b) acc[b] = f32x16{};
 
   const int tstart = (rstart / BQ) * BQ;
-  const int ntr = (j0 < s_kv && rend >= rstart) ? (rend - tstart) / BQ + 1 : 0;
+  // this chunk's row tiles [clo, chi] (tile = BQ rows), chunks counted down
+  // from the last tile; with one chunk, every tile of [rstart, rend]
+  const int tlast = (s_q - 1) / BQ;
+  const int clo = max(tstart / BQ, tlast - (cch + 1) * pr.cht + 1);
+  const int chi = min(rend / BQ, tlast - cch * pr.cht);
+  const int ntr = (j0 < s_kv && rend >= rstart && chi >= clo) ? chi - clo + 1 : 0;
   const int nt = ntr * g;
 
   // Tile order: query tiles from the END of the sequence downwards, the heads
@@ -221,7 +234,7 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
   // (row tile, head) at about the same time, whatever its key block, so the
   // tiles are shared through L2 instead of each workgroup streaming its own
   // row range.
-  auto tile_row = [&](int it) { return tstart + (ntr - 1 - it / g) * BQ; };
+  auto tile_row = [&](int it) { return (chi - it / g) * BQ; };
   // One tile = Q and dO (64 rows x 2d bytes: 64 / RPP wave-loads of 1 KiB,
   // RPP rows each, per tensor) plus the 64 LSE and D values. Rows past the end
   // read the last row: every load is unconditional and such rows are always
@@ -412,9 +425,40 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
     __syncthreads();
   }
 
-  if (key < s_k)
-    store_rows<DB>(role == 0 ? pr.dv : pr.dk, ((int64_t)key * pr.hkv + kvh) * D + hl * 4, acc,
-               role == 0 ? 1.f : pr.scale, pr.grad_f32, pr.accum);
+  if (key < s_k) {
+    const int64_t off = ((int64_t)key * pr.hkv + kvh) * D + hl * 4;
+    const float f = role == 0 ? 1.f : pr.scale;
+    if (pr.part != nullptr) {  // this chunk's partial sum, into its own fp32 slice
+      const int64_t slice = (int64_t)s_k * pr.hkv * D;
+      store_rows<DB>(pr.part + (int64_t)(role * pr.n_ch + cch) * slice, off, acc, f, 1, 0);
+    } else {
+      store_rows<DB>(role == 0 ? pr.dv : pr.dk, off, acc, f, pr.grad_f32, pr.accum);
+    }
+  }
+}
+
+// dV and dK from the row chunks' partial sums, added in chunk order (the
+// result does not depend on scheduling). One thread per 4 values; n4 values
+// of 4 per tensor.
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restrict__ part,
+                                                          void* dv, void* dk, int64_t n4,
+                                                          int n_ch, int f32, int accum) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 * n4) return;
+  const int t = i >= n4 ? 1 : 0;  // 0: dV, 1: dK
+  const int64_t e = i - t * n4;
+  const f32x4* src = reinterpret_cast<const f32x4*>(part) + (int64_t)t * n_ch * n4 + e;
+  f32x4 acc = src[0];
+  for (int c = 1; c < n_ch; ++c) acc += src[(int64_t)c * n4];
+  void* out = t ? dk : dv;
+  if (f32) {
+    f32x4* o = reinterpret_cast<f32x4*>(out) + e;
+    if (accum) acc += *o;
+    *o = acc;
+  } else {
+    const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    reinterpret_cast<u32x2*>(out)[e] = v;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -622,6 +666,21 @@ constexpr int kDqKeys = 32;      // keys per dQ tile
 constexpr int kDkdvRows = 64;    // query rows per dK/dV tile
 constexpr int kDkdvGroups = 4;   // 32-key groups (wave pairs) per dK/dV workgroup
 
+// Row chunks per key block in the dK/dV kernel. When the key blocks alone give
+// fewer than 512 workgroups (short sequences: 64 at 8K tokens on one KV head)
+// most compute units would sit idle, so each key block's rows are split to
+// give about 1024 (key block, chunk) items, at most 16 chunks per block.
+int dkdv_row_chunks(int64_t s_q, int64_t s_k, int hkv) {
+  constexpr int keys = 32 * kDkdvGroups;
+  const int64_t items = (s_k + keys - 1) / keys * hkv;
+  if (items >= 512) return 1;
+  const int64_t tiles = (s_q + kDkdvRows - 1) / kDkdvRows;
+  int64_t n = (1024 + items - 1) / items;
+  n = n < tiles ? n : tiles;
+  n = n < 16 ? n : 16;
+  return n > 1 ? (int)n : 1;
+}
+
 template <int D, int HG>
 int launch_dq(const BwdParams& p, int g, hipStream_t stream) {
   constexpr int QROWS = 32 * (4 / HG);
@@ -635,7 +694,7 @@ int launch_dq(const BwdParams& p, int g, hipStream_t stream) {
 
 // D and LSE * log2(e), then dK/dV, then dQ, for head dim D
 template <int D>
-int bwd_launch(const BwdParams& p, const AttnArgs& a, float* dd, float* lse2) {
+int bwd_launch(const BwdParams& p, const AttnArgs& a, float* dd, float* lse2, float* part) {
   {
     const int64_t n = a.s_q * a.hq * (D / 8);
     TraceScope ts("attn_bwd_rowdot_bf16", a.stream);
@@ -647,11 +706,27 @@ int bwd_launch(const BwdParams& p, const AttnArgs& a, float* dd, float* lse2) {
   }
   {
     constexpr int keys = 32 * kDkdvGroups;
-    dim3 grid((unsigned)((a.s_k + keys - 1) / keys), (unsigned)a.hkv);
-    TraceScope ts("attn_bwd_dkdv_bf16", a.stream);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kDkdvRows, kDkdvGroups>), grid,
-                       dim3(128 * kDkdvGroups), 0, a.stream, p);
-    if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
+    BwdParams pk = p;
+    pk.n_kb = (int)((a.s_k + keys - 1) / keys);
+    pk.n_ch = dkdv_row_chunks(a.s_q, a.s_k, a.hkv);
+    const int tiles = (int)((a.s_q + kDkdvRows - 1) / kDkdvRows);
+    pk.cht = (tiles + pk.n_ch - 1) / pk.n_ch;
+    pk.part = pk.n_ch > 1 ? part : nullptr;
+    dim3 grid((unsigned)(pk.n_kb * pk.n_ch), (unsigned)a.hkv);
+    {
+      TraceScope ts("attn_bwd_dkdv_bf16", a.stream);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, kDkdvRows, kDkdvGroups>), grid,
+                         dim3(128 * kDkdvGroups), 0, a.stream, pk);
+      if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
+    }
+    if (pk.n_ch > 1) {
+      const int64_t n4 = a.s_k * a.hkv * D / 4;
+      TraceScope ts("attn_bwd_dkdv_reduce", a.stream);
+      hipLaunchKernelGGL(dkdv_reduce_kernel, dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256), 0,
+                         a.stream, static_cast<const float*>(part), a.dv, a.dk, n4, pk.n_ch,
+                         a.out_f32, a.accumulate);
+      if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
+    }
   }
   const int g = a.hq / a.hkv;
   if (g % 4 == 0) return launch_dq<D, 4>(p, g, a.stream);
@@ -664,10 +739,10 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 }  // namespace
 
 size_t attn_bwd_bf16_workspace(int64_t s_q, int64_t s_k, int hq, int hkv, int d) {
-  (void)s_k;
-  (void)hkv;
-  (void)d;
-  return align256((size_t)hq * (size_t)kmajor_len(s_q) * 4) * 2;
+  // D and LSE*log2(e) per query row and head, then the dK/dV row-chunk partials
+  const size_t rows = align256((size_t)hq * (size_t)kmajor_len(s_q) * 4) * 2;
+  const int n_ch = dkdv_row_chunks(s_q, s_k, hkv);
+  return rows + (n_ch > 1 ? (size_t)2 * n_ch * (size_t)s_k * hkv * d * 4 : 0);
 }
 
 int attn_bwd_bf16(const AttnArgs& a) {
@@ -675,6 +750,7 @@ int attn_bwd_bf16(const AttnArgs& a) {
   char* ws = static_cast<char*>(a.workspace);
   float* dd = reinterpret_cast<float*>(ws);
   float* lse2 = reinterpret_cast<float*>(ws + align256((size_t)a.hq * s_tq * 4));
+  float* part = reinterpret_cast<float*>(ws + 2 * align256((size_t)a.hq * s_tq * 4));
   BwdParams p{};
   p.q = static_cast<const __bf16*>(a.q);
   p.k = static_cast<const __bf16*>(a.k);
@@ -694,7 +770,7 @@ int attn_bwd_bf16(const AttnArgs& a) {
   p.accum = a.accumulate;
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
-  return a.d == 64 ? bwd_launch<64>(p, a, dd, lse2) : bwd_launch<128>(p, a, dd, lse2);
+  return a.d == 64 ? bwd_launch<64>(p, a, dd, lse2, part) : bwd_launch<128>(p, a, dd, lse2, part);
 }
 
 }  // namespace usp
