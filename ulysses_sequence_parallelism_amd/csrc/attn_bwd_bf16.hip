@@ -216,6 +216,11 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
   // them as possibly in flight inside the loop and makes every MFMA wait for
   // the next tile's loads too.
   __builtin_amdgcn_s_waitcnt(0);
+  // The S -> P -> dV waves issue ahead of their dP -> dS -> dK partners when
+  // both are ready (wave priority, reset when the wave ends): P is ready
+  // sooner and the dV chain keeps the matrix unit busy while the partner does
+  // the dS arithmetic.
+  if (__builtin_amdgcn_readfirstlane(role) == 0) __builtin_amdgcn_s_setprio(2);
   f32x16 acc[DB];  // dV^T (role 0) or dK^T (role 1): rows = d, cols = keys
 #pragma unroll
   for (int b = 0; b < DB; ++b) acc[b] = f32x16{};
