@@ -486,10 +486,9 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
   constexpr int KB = BN / 32;
   // one array per pipeline slot: the wait-count pass then sees that loads
   // into one slot do not alias reads of the other, and waits only at barriers
-  __shared__ __attribute__((aligned(16))) __bf16 lk0[BN * D], lk1[BN * D];
-  __shared__ __attribute__((aligned(16))) __bf16 lv0[BN * D], lv1[BN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 lkv[4][BN * D];  // K slots 0, 1, V slots 0, 1
   // filled only by direct loads, which this compiler does not count as stores
-  asm volatile("" ::"s"(&lk0[0]), "s"(&lk1[0]), "s"(&lv0[0]), "s"(&lv1[0]) : "memory");
+  asm volatile("" ::"s"(&lkv[0][0]) : "memory");
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hl = lane >> 5, ln = lane & 31;
@@ -541,8 +540,8 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
   const int wu = __builtin_amdgcn_readfirstlane(w);  // LDS destinations go to M0
   const uint32_t key_bytes = (uint32_t)pr.hkv * D * 2;
   auto load_tile = [&](int t0, int buf) {
-    const uint32_t dk = lds_addr(buf ? &lk1[0] : &lk0[0]);
-    const uint32_t dv = lds_addr(buf ? &lv1[0] : &lv0[0]);
+    const uint32_t dk = lds_addr(&lkv[buf][0]);
+    const uint32_t dv = lds_addr(&lkv[2 + buf][0]);
     const char* kb = reinterpret_cast<const char*>(pr.k) + (int64_t)kvh * (D * 2);
     const char* vb = reinterpret_cast<const char*>(pr.v) + (int64_t)kvh * (D * 2);
     const int q = lane / KC;  // key within the part; lane % KC is the LDS slot
@@ -559,13 +558,26 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
     }
   };
   // fragment read offsets (elements) within a tile
-  int kro[KK], troff[DB][2];
+  // LDS byte addresses of the lane's row-fragment and transposed reads in
+  // the first K slot, opaque to the compiler: every read of a slot or block
+  // is then one of these registers plus a constant offset (with element
+  // offsets the compiler formed each address anew, or kept one per slot)
+  uint32_t kra[KK], tra[DB][2];
+  {
+    const uint32_t b0 = lds_addr(&lkv[0][0]);
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) kro[kk] = ln * D + (((hl + 2 * kk) ^ swz_row<D>(ln)) << 3);
+    for (int kk = 0; kk < KK; ++kk) {
+      kra[kk] = b0 + 2 * (ln * D + (((hl + 2 * kk) ^ swz_row<D>(ln)) << 3));
+      asm volatile("" : "+v"(kra[kk]));
+    }
 #pragma unroll
-  for (int b = 0; b < DB; ++b)
+    for (int b = 0; b < DB; ++b)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) troff[b][h] = tr_offset<D>(lane, b, h);
+      for (int h = 0; h < 2; ++h) {
+        tra[b][h] = b0 + 2 * tr_offset<D>(lane, b, h);
+        asm volatile("" : "+v"(tra[b][h]));
+      }
+  }
 
   if (nt > 0) load_tile(tstart, 0);
   wait_lds_dma();
@@ -583,16 +595,16 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         // the A fragments of each chain are requested before the chain runs
-        const __bf16* kp = (buf ? &lk1[0] : &lk0[0]) + kb * 32 * D;
-        const __bf16* vp = (buf ? &lv1[0] : &lv0[0]) + kb * 32 * D;
+        const uint32_t ko = (uint32_t)(buf * BN * D + kb * 32 * D) * 2;        // K slot
+        const uint32_t vo = (uint32_t)((2 + buf) * BN * D + kb * 32 * D) * 2;  // V slot
         bf16x8 afk[KK], afv[KK];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) afk[kk] = *reinterpret_cast<const bf16x8*>(kp + kro[kk]);
+        for (int kk = 0; kk < KK; ++kk) afk[kk] = lds_read_b128(kra[kk] + ko);
         sa[kb] = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) sa[kb] = mfma32(afk[kk], qreg[kk], sa[kb]);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) afv[kk] = *reinterpret_cast<const bf16x8*>(vp + kro[kk]);
+        for (int kk = 0; kk < KK; ++kk) afv[kk] = lds_read_b128(kra[kk] + vo);
         pa[kb] = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) pa[kb] = mfma32(afv[kk], doreg[kk], pa[kb]);
@@ -612,12 +624,12 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
       // that its vector work covers their latency
       bf16x8 kft[DB][2 * KB];
       {
-        const __bf16* kt = buf ? &lk1[0] : &lk0[0];
+        constexpr uint32_t ko = (uint32_t)(buf * BN * D) * 2;
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
           for (int ch = 0; ch < 2 * KB; ++ch)
-            kft[b][ch] = frag_tr(kt + ch * 16 * D, troff[b][0], troff[b][1]);
+            kft[b][ch] = frag_tr_at(tra[b][0] + ko + ch * 16 * D * 2, tra[b][1] + ko + ch * 16 * D * 2);
       }
       // dS^T = P^T (dP^T - D); most tiles need no mask, so the mask test is
       // kept off their path

@@ -110,6 +110,13 @@ __device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint3
 }
 #pragma clang diagnostic pop
 __device__ __forceinline__ void wait_lds_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Transposed read (see lds_read_tr) of the pair at byte addresses a0, a1.
+__device__ __forceinline__ bf16x8 frag_tr_at(uint32_t a0, uint32_t a1) {
+  typedef __attribute__((address_space(3))) bf16x4_v* lp;
+  const bf16x4_v a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lp)(uintptr_t)a0);
+  const bf16x4_v b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lp)(uintptr_t)a1);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 // 16-byte LDS read at byte address a. With a = base + constant, the constant
 // goes into the instruction's 16-bit offset field when it fits.
 __device__ __forceinline__ bf16x8 lds_read_b128(uint32_t a) {
