@@ -162,15 +162,16 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
   static_assert(BQ == 64, "the direct-load tile mapping assumes 64-row tiles");
   constexpr int MB = BQ / 32;          // 32-row blocks per tile
   constexpr int NCH = 2 * MB;          // 16-row chunks per tile
-  __shared__ __attribute__((aligned(16))) __bf16 lq[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) __bf16 ldo[2][BQ * D];
+  // Q in slots 0, 1 and dO in slots 2, 3 of one array: the phase-1 and phase-2
+  // reads of either tensor are then a fixed register plus a constant
+  __shared__ __attribute__((aligned(16))) __bf16 lqo[4][BQ * D];
   __shared__ __attribute__((aligned(16))) float llse[2][BQ];
   __shared__ __attribute__((aligned(16))) float ldd[2][BQ];
   __shared__ __attribute__((aligned(16))) u32x4 lp[KG][NCH][64];
   // These arrays are filled only by direct global->LDS loads, which this
   // compiler does not count as stores to them: without the escape below it
   // treats every read of them as undefined and deletes the dependent work.
-  asm volatile("" ::"s"(&lq[0][0]), "s"(&ldo[0][0]), "s"(&llse[0][0]), "s"(&ldd[0][0])
+  asm volatile("" ::"s"(&lqo[0][0]), "s"(&llse[0][0]), "s"(&ldd[0][0])
                : "memory");
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
     const int r0 = tile_row(it);
     const int p0 = (r1 % HALF) * PARTS;
     const char* base = reinterpret_cast<const char*>(r1 < HALF ? pr.q : pr.dout) + (int64_t)h * (D * 2);
-    const uint32_t dst = lds_addr(r1 < HALF ? &lq[buf][0] : &ldo[buf][0]);
+    const uint32_t dst = lds_addr(&lqo[r1 < HALF ? buf : 2 + buf][0]);
     // the lane's byte offset from the first row of a part: row lane / KC,
     // swizzled chunk
     const int q = lane / KC;
@@ -292,22 +293,36 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
   };
   // per-lane LDS element offsets of the row-fragment reads and of the
   // transposed reads (column block b, half h) within a tile
-  int roff[KK], troff[DB][2];
+  // as LDS byte addresses in slot 0 of the tensor the wave reads (phase 1: Q
+  // for role 0, dO for role 1; phase 2 the other), opaque to the compiler so
+  // that a slot and block offset is a constant in the read's offset field
+  uint32_t ra1[KK], ra2[DB][2];
+  {
+    const int rolu = __builtin_amdgcn_readfirstlane(role);
+    const uint32_t b0 = lds_addr(&lqo[0][0]), dob = 2 * BQ * D * 2;  // dO slot 0
+    const uint32_t b1 = b0 + (rolu == 0 ? 0u : dob), b2 = b0 + (rolu == 0 ? dob : 0u);
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) roff[kk] = ln * D + (((hl + 2 * kk) ^ swz_row<D>(ln)) << 3);
+    for (int kk = 0; kk < KK; ++kk) {
+      ra1[kk] = b1 + 2 * (ln * D + (((hl + 2 * kk) ^ swz_row<D>(ln)) << 3));
+      asm volatile("" : "+v"(ra1[kk]));
+    }
 #pragma unroll
-  for (int b = 0; b < DB; ++b)
+    for (int b = 0; b < DB; ++b)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) troff[b][h] = tr_offset<D>(lane, b, h);
+      for (int h = 0; h < 2; ++h) {
+        ra2[b][h] = b2 + 2 * tr_offset<D>(lane, b, h);
+        asm volatile("" : "+v"(ra2[b][h]));
+      }
+  }
 
   if (nt > 0) load_tile(0, 0);
   wait_lds_dma();
   __syncthreads();
 
-  for (int it = 0; it < nt; ++it) {
-    const int buf = it & 1;
-    const __bf16* tq = lq[buf];
-    const __bf16* tdo = ldo[buf];
+  // one tile; the loop below is unrolled by two so that the slot is a
+  // compile-time constant
+  auto tile = [&](int it, auto parity) {
+    constexpr int buf = decltype(parity)::value;  // == it & 1
     const float* tlse = llse[buf];
     const float* tdd = ldd[buf];
     // the next tile into the other slot, whose last reads were in the previous
@@ -320,15 +335,14 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
     f32x16 pa[MB];
     bf16x8 pb[NCH];
     if (active) {
-      const __bf16* base = role == 0 ? tq : tdo;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         // all 8 A fragments of the block are requested before its MFMA chain,
         // so the chain waits for one LDS round trip, not one per MFMA pair
-        const __bf16* ap = base + mb * 32 * D;
         bf16x8 af[KK];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) af[kk] = *reinterpret_cast<const bf16x8*>(ap + roff[kk]);
+        for (int kk = 0; kk < KK; ++kk)
+          af[kk] = lds_read_b128(ra1[kk] + (uint32_t)(buf * BQ * D + mb * 32 * D) * 2);
         __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the chain
         pa[mb] = f32x16{};
 #pragma unroll
@@ -400,7 +414,6 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
         }
       }
       // dO^T (role 0) or Q^T (role 1): transposed reads of the row tile
-      const __bf16* tbase = role == 0 ? tdo : tq;
       bf16x8 af[DB][NCH];
 #pragma unroll
       for (int b2 = 0; b2 < DB; b2 += 2) {
@@ -408,7 +421,8 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
           for (int ch = 0; ch < NCH; ++ch)
-            af[b2 + bb][ch] = frag_tr(tbase + ch * 16 * D, troff[b2 + bb][0], troff[b2 + bb][1]);
+            af[b2 + bb][ch] = frag_tr_at(ra2[b2 + bb][0] + (uint32_t)(buf * BQ * D + ch * 16 * D) * 2,
+                                         ra2[b2 + bb][1] + (uint32_t)(buf * BQ * D + ch * 16 * D) * 2);
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
@@ -428,7 +442,13 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
     }
     wait_lds_dma();  // the next tile has landed (only the loading waves wait)
     __syncthreads();
+  };
+  int it = 0;
+  for (; it + 2 <= nt; it += 2) {
+    tile(it, std::integral_constant<int, 0>{});
+    tile(it + 1, std::integral_constant<int, 1>{});
   }
+  if (it < nt) tile(it, std::integral_constant<int, 0>{});
 
   if (key < s_k) {
     const int64_t off = ((int64_t)key * pr.hkv + kvh) * D + hl * 4;
