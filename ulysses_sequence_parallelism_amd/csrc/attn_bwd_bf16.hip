@@ -319,15 +319,19 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
   wait_lds_dma();
   __syncthreads();
 
-  // one tile; the loop below is unrolled by two so that the slot is a
-  // compile-time constant
-  auto tile = [&](int it, auto parity) {
+  // one tile of role R; the loop below is unrolled by two so that the slot is
+  // a compile-time constant, and instantiated per role so that each wave runs
+  // straight-line code for its own role (with the role as a run-time branch
+  // this compiler joined P, dS and the accumulators with register copies)
+  auto tile = [&](int it, auto parity, auto role_c) __attribute__((always_inline)) {
     constexpr int buf = decltype(parity)::value;  // == it & 1
+    constexpr int R = decltype(role_c)::value;    // == role
     const float* tlse = llse[buf];
     const float* tdd = ldd[buf];
     // the next tile into the other slot, whose last reads were in the previous
     // tile; the barrier at the end of this tile waits for it
-    if (it + 1 < nt) load_tile(it + 1, buf ^ 1);
+    if constexpr (R == 1)
+      if (it + 1 < nt) load_tile(it + 1, buf ^ 1);
     const int r0 = tile_row(it);
     const bool active = wave_live && r0 + BQ - 1 >= wr_lo && r0 <= wr_hi;
 
@@ -348,7 +352,7 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) pa[mb] = mfma32(af[kk], sreg[kk], pa[mb]);
       }
-      if (role == 0) {
+      if constexpr (R == 0) {
         // P = exp2(S*scale*log2e - LSE*log2e); masked entries are 0. Most
         // tiles need no mask, so the mask test is kept off their path.
         const bool full = all_keys_valid && r0 >= free_lo && r0 + BQ - 1 <= free_hi;
@@ -391,7 +395,7 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
 
     // phase 2: role 0 -> dV^T += dO^T P; role 1 -> dS, dK^T += Q^T dS
     if (active) {
-      if (role == 1) {
+      if constexpr (R == 1) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -443,12 +447,16 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
     wait_lds_dma();  // the next tile has landed (only the loading waves wait)
     __syncthreads();
   };
-  int it = 0;
-  for (; it + 2 <= nt; it += 2) {
-    tile(it, std::integral_constant<int, 0>{});
-    tile(it + 1, std::integral_constant<int, 1>{});
-  }
-  if (it < nt) tile(it, std::integral_constant<int, 0>{});
+  auto run = [&](auto role_c) __attribute__((always_inline)) {
+    int it = 0;
+    for (; it + 2 <= nt; it += 2) {
+      tile(it, std::integral_constant<int, 0>{}, role_c);
+      tile(it + 1, std::integral_constant<int, 1>{}, role_c);
+    }
+    if (it < nt) tile(it, std::integral_constant<int, 0>{}, role_c);
+  };
+  if (__builtin_amdgcn_readfirstlane(role) == 0) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
 
   if (key < s_k) {
     const int64_t off = ((int64_t)key * pr.hkv + kvh) * D + hl * 4;
