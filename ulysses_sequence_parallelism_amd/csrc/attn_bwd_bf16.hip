@@ -512,9 +512,11 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
   constexpr int PPW = BN / RPP / 4;  // wave-loads per wave, tensor and tile
   constexpr int QROWS = 32 * (4 / HG);
   constexpr int KB = BN / 32;
-  // one array per pipeline slot: the wait-count pass then sees that loads
-  // into one slot do not alias reads of the other, and waits only at barriers
-  __shared__ __attribute__((aligned(16))) __bf16 lkv[4][BN * D];  // K slots 0, 1, V slots 0, 1
+  // K slots 0, 1 and V slots 0, 1 in one array, so that every slot sits at a
+  // fixed offset from the first (the fragment reads below add it as a
+  // constant); the direct loads are inline asm, which the wait-count pass does
+  // not see, so sharing an array costs no waits
+  __shared__ __attribute__((aligned(16))) __bf16 lkv[4][BN * D];
   // filled only by direct loads, which this compiler does not count as stores
   asm volatile("" ::"s"(&lkv[0][0]) : "memory");
 

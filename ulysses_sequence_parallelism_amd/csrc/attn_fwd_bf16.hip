@@ -88,17 +88,14 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
   constexpr int VPW = D / 8 / 8;     // V^T wave-loads (8 d-rows each) per wave and tile
   constexpr int QBW = 8 / HG;
   constexpr int QROWS = 32 * QBW;
-  // one array per slot: the wait-count pass cannot tell two slots of one
-  // array apart and would otherwise wait for the next tiles' loads before
-  // every read of the current ones
-  __shared__ __attribute__((aligned(16))) __bf16 lk0[BN * D];
-  __shared__ __attribute__((aligned(16))) __bf16 lk1[BN * D];
-  __shared__ __attribute__((aligned(16))) __bf16 lv0[D * BN];
-  __shared__ __attribute__((aligned(16))) __bf16 lv1[D * BN];
+  // two slots per tensor in one array each, so that slot 1 sits exactly one
+  // tile after slot 0 (the fragment reads below add that as a constant)
+  __shared__ __attribute__((aligned(16))) __bf16 lk[2][BN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 lv[2][D * BN];
   // filled only by direct loads, which this compiler does not count as stores
-  asm volatile("" ::"s"(&lk0[0]), "s"(&lk1[0]), "s"(&lv0[0]), "s"(&lv1[0]) : "memory");
-  auto kslot = [&](int b) -> __bf16* { return b ? &lk1[0] : &lk0[0]; };
-  auto vslot = [&](int b) -> __bf16* { return b ? &lv1[0] : &lv0[0]; };
+  asm volatile("" ::"s"(&lk[0][0]), "s"(&lv[0][0]) : "memory");
+  auto kslot = [&](int b) -> __bf16* { return &lk[b][0]; };
+  auto vslot = [&](int b) -> __bf16* { return &lv[b][0]; };
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hl = lane >> 5, ln = lane & 31;
@@ -193,7 +190,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
   // the compiler kept more address registers and spilled.
   uint32_t kra[KK], vra[4];
   {
-    const uint32_t kb0 = lds_addr(&lk0[0]), vb0 = lds_addr(&lv0[0]);
+    const uint32_t kb0 = lds_addr(&lk[0][0]), vb0 = lds_addr(&lv[0][0]);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       kra[kk] = kb0 + 2 * (ln * D + (((hl + 2 * kk) ^ swz_row<D>(ln)) << 3));
