@@ -123,7 +123,10 @@ int usp_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int hq, int hkv, int d, float softmax_scale, int causal, int dtype,
                  void* stream);
 
-/* Workspace bytes usp_attn_bwd needs for these sizes. */
+/* Workspace bytes usp_attn_bwd needs for these sizes: per (query head, row)
+ * fp32 D and LSE values and, for bf16 on short sequences (fewer than 512
+ * blocks of 128 keys over all KV heads), fp32 partial dK and dV per row
+ * chunk; deterministic in the sizes. */
 size_t usp_attn_bwd_workspace_bytes(int64_t s_pad, int hq, int hkv, int d, int dtype);
 
 /*
@@ -201,7 +204,8 @@ int usp_attn_fwd_interval(const void* q, const void* k, const void* v, void* o, 
 int usp_attn_merge(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
                    void* o, float* lse, int64_t s_q, int hq, int d, int o_dtype, void* stream);
 
-/* Workspace bytes usp_attn_bwd_interval needs for these sizes. */
+/* Workspace bytes usp_attn_bwd_interval needs for these sizes (as for
+ * usp_attn_bwd, with s_q query rows and s_k keys). */
 size_t usp_attn_bwd_interval_workspace_bytes(int64_t s_q, int64_t s_k, int hq, int hkv, int d,
                                              int dtype);
 
