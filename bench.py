@@ -85,13 +85,13 @@ KERNELS = {
 }
 
 
-def traffic_for(kernel: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter summaries
-    (profiles/traffic_<kernel>_<workload>.txt), or None when absent or taken
-    on a different version of the kernel source."""
+def counter_summary(kernel: str, workload: str) -> dict:
+    """Key/value pairs of the committed rocprofv3 counter summary
+    (profiles/traffic_<kernel>_<workload>.txt), or {} when absent or taken on
+    a different version of the kernel source."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path) or kernel not in KERNELS:
-        return None
+        return {}
     kv = {}
     with open(path) as f:
         for line in f:
@@ -99,9 +99,14 @@ def traffic_for(kernel: str, workload: str):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
     if kv.get("source_hash") != src_hash(*KERNELS[kernel][0]):
-        return None
+        return {}
+    return kv
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the counter summary, or None."""
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(counter_summary(kernel, workload)["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -452,6 +457,14 @@ def main():
                 "traffic": traffic_for(dom["name"], w.name),
                 "avg_launch_ms": round(dom_avg_ms, 4),
                 "algorithmic_flop_per_launch": dom_flops}
+    # the same kernel against the peak at the clock it ran at in the counter
+    # run (the chip is power-limited below 2.4 GHz under this load)
+    cs = counter_summary(dom["name"], w.name)
+    if "clock_ghz" in cs:
+        clk = float(cs["clock_ghz"])
+        roofline["counter_clock_ghz"] = round(clk, 3)
+        roofline["counter_mfma_busy"] = round(float(cs["mfma_busy"]), 3)
+        roofline["frac_at_counter_clock"] = round(achieved / (PEAK_BF16_TFLOPS * clk / 2.4), 4)
 
     # ---- composite permute bandwidth (all P ranks' Q, K, V; not part of the step).
     # Passes rotate over n_sets buffer sets with n_sets * bytes >= 1 GiB, four
