@@ -64,6 +64,11 @@ SMALL = [
     ("d64_docs", 2100, 2100, 4, 1, [0, 100, 101, 1000, 1377, 2100], True, 64),
     ("d64_bidir_padded", 500, 490, 8, 2, None, False, 64),
     ("d64_tiny_17", 17, 17, 4, 1, None, True, 64),
+    # several KV heads at a size where every kernel runs a full grid
+    ("w8_ragged_16q4kv", 4100, 4100, 16, 4, None, True),
+    ("w8_docs_16q4kv", 4500, 4500, 16, 4, [0, 1000, 1001, 3000, 4500], True),
+    ("w8_bidir_padded_16q4kv", 4160, 4150, 16, 4, None, False),
+    ("w8_d64_16q4kv", 4100, 4100, 16, 4, None, True, 64),
 ]
 
 
