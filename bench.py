@@ -184,8 +184,18 @@ def interval_path(args, w, dev, share, full):
     torch.cuda.synchronize()
     ws_f = torch.empty(usp.usp_attn_fwd_workspace_bytes(s_pad, hq, hkv, d, 0), dtype=torch.uint8,
                        device=dev)
-    ws_b = torch.empty(usp.usp_attn_bwd_workspace_bytes(s_pad, hq, hkv, d, 0), dtype=torch.uint8,
-                       device=dev)
+    # backward scratch for the largest call this layout makes (a short
+    # interval can need more than the whole share: dK/dV row-chunk partials)
+    if args.path == "ring":
+        nb = usp.usp_attn_bwd_interval_workspace_bytes(s_pad // args.ring, s_pad // args.ring, hq,
+                                                       hkv, d, 0)
+    elif args.path == "cp":
+        a_cp = s_pad * (args.cp - 1) // args.cp
+        nb = usp.usp_attn_bwd_interval_workspace_bytes(s_pad - a_cp, s_pad, hq, hkv, d, 0)
+    else:
+        nb = 0
+    nb = max(nb, usp.usp_attn_bwd_workspace_bytes(s_pad, hq, hkv, d, 0))
+    ws_b = torch.empty(nb, dtype=torch.uint8, device=dev)
     if args.path == "ring":
         blk = s_pad // r
         qa, qb = (r - 1) * blk, s_pad                      # the last ring rank's query rows
