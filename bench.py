@@ -298,7 +298,7 @@ def interval_path(args, w, dev, share, full):
     step_ms = ev0.elapsed_time(ev1) / args.steps
     per = {e["name"]: e for e in trace}
     f_fwd, f_bwd = 4 * d * hq * pairs_alg, 10 * d * hq * pairs_alg
-    fwd_names = ("attn_fwd_kmajor_v", "attn_fwd_bf16", "attn_merge")
+    fwd_names = ("attn_fwd_kmajor_v", "attn_fwd_bf16", "attn_fwd_merge", "attn_merge")
     fwd_ms = sum(per[n]["total_ms"] for n in fwd_names if n in per) / args.steps
     bwd_ms = sum(e["total_ms"] for e in trace if e["name"] not in fwd_names) / args.steps
     # dominant kernel: its algorithmic FLOPs summed over its launches / its summed time
@@ -452,7 +452,7 @@ def main():
     def kms(*names):
         return sum(per[n]["total_ms"] for n in names if n in per) / args.steps
 
-    fwd_ms = kms("attn_fwd_kmajor_v", "attn_fwd_bf16")
+    fwd_ms = kms("attn_fwd_kmajor_v", "attn_fwd_bf16", "attn_fwd_merge")
     bwd_ms = kms("attn_bwd_kmajor", "attn_bwd_rowdot_bf16", "attn_bwd_dkdv_bf16",
                  "attn_bwd_dkdv_reduce", "attn_bwd_dq_bf16")
     perm_ms = kms("pack_seq2head", "unpack_head2seq")
@@ -540,6 +540,9 @@ def main():
                    "head_dim": d, "causal": True},
         "attn_fwd_ms": round(fwd_ms, 3),
         "attn_bwd_ms": round(bwd_ms, 3),
+        # key splits of the forward (1: one pass; more on short sequences)
+        "attn_fwd_key_splits": usp.usp_attn_fwd_num_splits(
+            s_pad, s_pad, hq, hkv, d, 0, s_k_valid=w.s, workspace_bytes=ws_f.numel()),
         "attn_fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 1),
         "attn_fwd_bwd_tflops": round((f_fwd + f_bwd) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 1),
         "attn_fwd_frac_of_peak": round(f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),

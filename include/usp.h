@@ -91,7 +91,12 @@ int usp_unpack_head2seq(const void* y, void* x, int64_t s_real, int p, int h, in
 
 /*
  * Workspace bytes usp_attn_fwd needs (0 for USP_FP32). The bf16 path stores a
- * key-major copy of V there.
+ * key-major copy of V there and, when s_pad rows make a grid of fewer than 512
+ * workgroups (short sequences), room for up to 8 key splits: fp32 partial O
+ * and LSE of every query row, combined exactly by a merge kernel (see
+ * usp_attn_fwd_num_splits). About 135 MB at s_pad = 8192 with 4 query heads and
+ * d = 128; nothing beyond the V copy from 16,384 query rows per KV head at 4:1
+ * GQA upwards.
  */
 size_t usp_attn_fwd_workspace_bytes(int64_t s_pad, int hq, int hkv, int d, int dtype);
 
@@ -110,7 +115,11 @@ size_t usp_attn_fwd_workspace_bytes(int64_t s_pad, int hq, int hkv, int d, int d
  *     = s_pad, or NULL. Its contents are not checked (device memory); values
  *     outside [0, s_pad] are clamped, never dereferenced out of range.
  *   workspace: device memory of usp_attn_fwd_workspace_bytes() bytes (may be
- *     NULL when that is 0); contents are scratch.
+ *     NULL when that is 0); contents are scratch. For bf16 the V copy,
+ *     hkv * d * round_up(s_pad, 128) * 2 bytes, is the minimum; with less room
+ *     than the query returns the call runs fewer key splits (one pass with
+ *     none), same results up to rounding. The whole workspace_bytes range must
+ *     not overlap the other arguments.
  * Supported: d in {64, 128}, both dtypes.
  * Errors: USP_ERR_INVALID for s_valid < 1 or > s_pad, hq % hkv != 0,
  * cu_seqlens with s_valid != s_pad or n_docs < 1, misalignment, aliasing;
@@ -173,7 +182,9 @@ int usp_attn_bwd(const void* q, const void* k, const void* v, const void* o,
  *     USP_BF16 allowed for bf16 inputs); lse: [hq][s_q] fp32. Both overwritten.
  *   cu_seqlens: device int32 [n_docs + 1], 0 = cu[0] <= ... <= cu[n_docs], and
  *     cu[n_docs] >= q_off + s_q and >= k_off + s_k; or NULL. Not checked.
- *   workspace: usp_attn_fwd_workspace_bytes(s_k, hq, hkv, d, dtype) bytes.
+ *   workspace: usp_attn_fwd_workspace_bytes(s_k, hq, hkv, d, dtype) bytes, at
+ *     least the V copy as in usp_attn_fwd (room for the key splits of s_q rows
+ *     when s_q > s_k may need more; with less the call splits less).
  * Errors: USP_ERR_INVALID for s_q < 1, s_k < 1, negative offsets,
  * q_off + s_q or k_off + s_k >= 2^30, s_k_valid outside [0, s_k], the head and
  * scale checks of usp_attn_fwd, misalignment or aliasing; USP_ERR_UNSUPPORTED
@@ -185,6 +196,23 @@ int usp_attn_fwd_interval(const void* q, const void* k, const void* v, void* o, 
                           int64_t s_k_valid, const int32_t* cu_seqlens, int n_docs,
                           int hq, int hkv, int d, float softmax_scale, int causal, int dtype,
                           int o_dtype, void* stream);
+
+/*
+ * Number of key splits usp_attn_fwd / usp_attn_fwd_interval run for these
+ * arguments with a workspace of workspace_bytes bytes (1: a single pass).
+ * With n > 1 splits each query block's key tiles are cut into n consecutive
+ * ranges processed by separate workgroups (so a short sequence fills the
+ * chip and the long rows of the causal triangle are shared out); each writes
+ * an fp32 partial O and LSE into the workspace and a merge kernel combines
+ * them exactly (the identity of usp_attn_merge), then writes o and lse. The
+ * plan depends only on these arguments (not on cu_seqlens' contents or the
+ * data), so a call is deterministic. Host-only: no device is touched.
+ * Returns the count, or the error usp_attn_fwd_interval would return for
+ * these sizes (USP_ERR_INVALID, USP_ERR_UNSUPPORTED).
+ */
+int usp_attn_fwd_num_splits(int64_t s_q, int64_t q_off, int64_t s_k, int64_t k_off,
+                            int64_t s_k_valid, int hq, int hkv, int d, int causal, int dtype,
+                            size_t workspace_bytes);
 
 /*
  * Exact merge of two partial results over disjoint key sets of the same query

@@ -130,6 +130,8 @@ def test_attention_argument_errors(L, f):
     assert f(L, ws=0) == WORKSPACE
     assert f(L, ws_bytes=16) == WORKSPACE
     assert f(L, ws=(3 << 30) + 8) == INVALID            # misaligned workspace
+    if f is fwd:  # the forward needs its V copy (128 x 256 x 2 bytes) at least
+        assert f(L, ws_bytes=128 * 256 * 2 - 16) == WORKSPACE
 
 
 def test_attention_null_and_alias(L):
@@ -258,6 +260,51 @@ def test_workspace_sizes(L):
     assert L.usp_attn_bwd_interval_workspace_bytes(512, 512, 4, 1, 128, BF16) == \
         L.usp_attn_bwd_workspace_bytes(512, 4, 1, 128, BF16)
     assert L.usp_attn_bwd_interval_workspace_bytes(300, 700, 4, 2, 64, FP32) == 300 * 4 * 4
+
+
+def fwd_split_cap(s, hq, hkv):
+    """Most key splits the bf16 forward may run for s query rows: 1 when the
+    unsplit grid (workgroups of HG query heads x 8/HG blocks of 32 rows) has
+    512 workgroups or more, else enough for about 1024, at most 8."""
+    g = hq // hkv
+    hg = 4 if g % 4 == 0 else 2 if g % 2 == 0 else 1
+    wgs = -(-s // (32 * (8 // hg))) * hkv * (g // hg)
+    return 1 if wgs >= 512 else min(8, -(-1024 // wgs))
+
+
+def test_fwd_workspace_and_key_splits(L):
+    vcopy = lambda s, hkv, d: hkv * d * ((s + 127) // 128 * 128) * 2
+    for s, hq, hkv, d in ((8192, 4, 1, 128), (16384, 4, 1, 128), (16385, 4, 1, 128),
+                          (32768, 4, 1, 128), (1000, 8, 2, 64), (120000, 4, 1, 128),
+                          (131072, 16, 4, 128), (64, 4, 1, 128)):
+        z = fwd_split_cap(s, hq, hkv)
+        # fp32 partial O (256-byte aligned) and LSE per split
+        room = (-(-z * s * hq * d * 4 // 256) * 256 + z * hq * s * 4) if z > 1 else 0
+        ws = L.usp_attn_fwd_workspace_bytes(s, hq, hkv, d, BF16)
+        assert ws == vcopy(s, hkv, d) + room
+        for causal in (0, 1):
+            n = L.usp_attn_fwd_num_splits(s, 0, s, 0, s, hq, hkv, d, causal, BF16, ws)
+            assert 1 <= n <= z
+            # deterministic, and one pass without room for the partials
+            assert n == L.usp_attn_fwd_num_splits(s, 0, s, 0, s, hq, hkv, d, causal, BF16, ws)
+            assert L.usp_attn_fwd_num_splits(s, 0, s, 0, s, hq, hkv, d, causal, BF16,
+                                             vcopy(s, hkv, d)) == 1
+            assert L.usp_attn_fwd_num_splits(s, 0, s, 0, s, hq, hkv, d, causal, FP32, ws) == 1
+    split = lambda *a: L.usp_attn_fwd_num_splits(*a, L.usp_attn_fwd_workspace_bytes(
+        a[2], a[5], a[6], a[7], BF16))
+    # the short causal share (128 workgroups, a 128-tile triangle) is split; the
+    # long ones, and the contiguous context-parallel rank, run one pass
+    assert split(8192, 0, 8192, 0, 8192, 4, 1, 128, 1, BF16) > 1
+    assert split(16384, 0, 16384, 0, 16384, 4, 1, 128, 1, BF16) > 1
+    for s in (32768, 120000):
+        assert split(s, 0, s, 0, s, 4, 1, 128, 1, BF16) == 1
+    assert split(15000, 105000, 120000, 0, 120000, 4, 1, 128, 1, BF16) == 1
+    # fewer than 8 tiles per split: one pass
+    assert split(300, 0, 300, 0, 300, 4, 1, 128, 1, BF16) == 1
+    # argument errors as in the interval forward
+    assert L.usp_attn_fwd_num_splits(0, 0, 8, 0, 8, 4, 1, 128, 1, BF16, 1 << 30) == -1
+    assert L.usp_attn_fwd_num_splits(8, 0, 8, 0, 8, 4, 1, 96, 1, BF16, 1 << 30) == -2
+    assert L.usp_attn_fwd_num_splits(8, 0, 8, 0, 9, 4, 1, 128, 1, BF16, 1 << 30) == -1
 
 
 def test_fast_division_host_side(tmp_path):

@@ -53,7 +53,10 @@
 //     a boundary; tiles entirely outside every row's range are never visited.
 //   * Workgroups are launched heaviest-first (last query block first) so the
 //     causal triangle's long rows start early and the tail is short.
+#include <algorithm>
+#include <queue>
 #include <type_traits>
+#include <vector>
 
 #include "usp_common.h"
 #include "usp_internal.h"
@@ -76,6 +79,11 @@ struct FwdParams {
   int64_t s_t;
   int hq, hkv, n_qblocks;
   float scale_log2;   // softmax scale * log2(e)
+  // Key splits: with n_split > 1 the workgroups of one query block share its
+  // tile range, split z taking tiles [z, z + 1) * split_tiles of it, and write
+  // fp32 partial O / LSE at o32 + z * o_split and lse + z * lse_split.
+  int n_split, split_tiles;
+  int64_t o_split, lse_split;
 };
 
 template <int D, int HG>
@@ -103,7 +111,9 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
   const int chunks = g / HG;
   const int kvh = blockIdx.y / chunks, hc = blockIdx.y % chunks;
   const int head = kvh * g + hc * HG + (w % HG);
-  const int qb = pr.n_qblocks - 1 - (int)blockIdx.x;  // heaviest first
+  // heaviest query block first; its key splits follow one another
+  const int qb = pr.n_qblocks - 1 - (int)blockIdx.x / pr.n_split;
+  const int zs = (int)blockIdx.x % pr.n_split;
   const int q0 = qb * QROWS;
   const int s_q = pr.m.s_q, s_k = pr.m.s_k;
   const int q1 = min(q0 + QROWS, s_q);
@@ -118,7 +128,11 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
   // workgroup key range and the range that needs no mask (both ends of a
   // row's range are nondecreasing in the row)
   const KeyRange kfirst = row_keys(pr.m, q0), klast = row_keys(pr.m, q1 - 1);
-  const int kmin = kfirst.lo, kmax = klast.hi;
+  // with key splits, the part of it in this split's tiles (tiles counted from
+  // the one holding the first key, as without splits)
+  const int t_split = (kfirst.lo / BN + zs * pr.split_tiles) * BN;
+  const int kmin = pr.n_split > 1 ? max(kfirst.lo, t_split) : kfirst.lo;
+  const int kmax = pr.n_split > 1 ? min(klast.hi, t_split + pr.split_tiles * BN - 1) : klast.hi;
   const int free_lo = klast.lo, free_hi = kfirst.hi;
   // this wave's key range (waves of one workgroup may cover different rows)
   const int wkmin = row_keys(pr.m, min(wq0, s_q - 1)).lo;
@@ -143,6 +157,12 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
 
   const int tstart = (kmin / BN) * BN;
   const int nt = kmax >= kmin ? (kmax - tstart) / BN + 1 : 0;
+  float* const o32 = pr.n_split > 1 ? pr.o32 + zs * pr.o_split : pr.o32;
+  float* const lse_out = pr.n_split > 1 ? pr.lse + zs * pr.lse_split : pr.lse;
+  if (pr.n_split > 1 && nt == 0) {  // nothing in this split: LSE = -inf tells the merge to skip it
+    if (row_ok && hl == 0) lse_out[(int64_t)head * s_q + qi] = -INFINITY;
+    return;
+  }
 
   // Software pipeline: the scores of tile t+1 are computed while tile t goes
   // through the softmax, so one wave's MFMAs and vector work are independent
@@ -334,14 +354,14 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int64_t ob = ((int64_t)qi * pr.hq + head) * D + hl * 4;
-    if (pr.o32 != nullptr) {
+    if (o32 != nullptr) {
 #pragma unroll
       for (int b = 0; b < DB; ++b)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           f32x4 v4 = {oacc[b][4 * r] * inv, oacc[b][4 * r + 1] * inv, oacc[b][4 * r + 2] * inv,
                       oacc[b][4 * r + 3] * inv};
-          *reinterpret_cast<f32x4*>(pr.o32 + ob + b * 32 + r * 8) = v4;
+          *reinterpret_cast<f32x4*>(o32 + ob + b * 32 + r * 8) = v4;
         }
     } else {
 #pragma unroll
@@ -354,8 +374,149 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
         }
     }
     if (hl == 0)
-      pr.lse[(int64_t)head * s_q + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      lse_out[(int64_t)head * s_q + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
+}
+
+// Exact combination of the key splits of one call. Split z covered a disjoint
+// range of key tiles and returned O_z normalised over its own keys and their
+// natural-log LSE_z; over the union, with M = max_z LSE_z and
+// w_z = exp(LSE_z - M),
+//     O = sum_z w_z O_z / sum_z w_z,   LSE = M + log(sum_z w_z)
+// (the same identity as the two-way merge of ring steps). A split whose LSE is
+// -inf saw no allowed key of the row; its O is not read (an empty split never
+// writes it). A row with no allowed key at all gets O = 0, LSE = -inf.
+// Memory-bound: one thread per 8 consecutive values of one (row, head).
+template <int D>
+__global__ __launch_bounds__(256) void split_merge_kernel(const float* part, const float* plse,
+                                                          int64_t o_split, int64_t lse_split,
+                                                          int nz, void* o, float* lse, int s_q,
+                                                          FastDiv hq, int n, int out_f32) {
+  constexpr int C = D / 8;  // threads per (row, head)
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= n) return;
+  const int rh = t / C, c = t % C;
+  const uint32_t i = hq.div((uint32_t)rh);
+  const int h = rh - (int)(i * hq.d);
+  const int64_t li = (int64_t)h * s_q + i;
+  float m = -INFINITY;
+  for (int z = 0; z < nz; ++z) m = fmaxf(m, plse[z * lse_split + li]);
+  const int64_t e = (int64_t)rh * D + c * 8;
+  f32x4 a0 = {}, a1 = {};
+  float l_out = -INFINITY;
+  if (m != -INFINITY) {
+    float ws = 0.f;
+    for (int z = 0; z < nz; ++z) {
+      const float lz = plse[z * lse_split + li];
+      if (lz == -INFINITY) continue;
+      const float wz = expf(lz - m);
+      const float* pz = part + z * o_split + e;
+      a0 += wz * *reinterpret_cast<const f32x4*>(pz);
+      a1 += wz * *reinterpret_cast<const f32x4*>(pz + 4);
+      ws += wz;
+    }
+    const float inv = 1.f / ws;  // ws >= 1: the split holding the maximum has weight 1
+    a0 *= inv;
+    a1 *= inv;
+    l_out = m + logf(ws);
+  }
+  if (out_f32) {
+    float* of = static_cast<float*>(o) + e;
+    *reinterpret_cast<f32x4*>(of) = a0;
+    *reinterpret_cast<f32x4*>(of + 4) = a1;
+  } else {
+    u32x4 v4 = {pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]), pack_bf16x2(a1[0], a1[1]),
+                pack_bf16x2(a1[2], a1[3])};
+    *reinterpret_cast<u32x4*>(static_cast<__bf16*>(o) + e) = v4;
+  }
+  if (c == 0) lse[li] = l_out;
+}
+
+int hg_for(int g) { return g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1; }
+
+// Query rows per workgroup and workgroups of the unsplit grid.
+int qrows_for(int hq, int hkv) { return 32 * (8 / hg_for(hq / hkv)); }
+int64_t grid_size(int64_t s_q, int hq, int hkv) {
+  const int g = hq / hkv;
+  return (s_q + qrows_for(hq, hkv) - 1) / qrows_for(hq, hkv) * hkv * (g / hg_for(g));
+}
+
+// Key splits pay off only while the unsplit grid is short of a few rounds of
+// workgroups on the 256 compute units (one 8-wave workgroup each).
+constexpr int kCUs = 256;
+constexpr int kMaxSplits = 8;
+constexpr int kMinSplitTiles = 8;
+int split_cap(int64_t s_q, int hq, int hkv) {
+  const int64_t wgs = grid_size(s_q, hq, hkv);
+  if (wgs >= 2 * kCUs) return 1;
+  return (int)std::min<int64_t>(kMaxSplits, (4 * kCUs + wgs - 1) / wgs);
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+size_t vcopy_bytes(int64_t s_k, int hkv, int d) { return (size_t)hkv * d * kmajor_len(s_k) * 2; }
+size_t split_bytes(int z, int64_t s_q, int hq, int d) {
+  return z > 1 ? align256((size_t)z * s_q * hq * d * 4) + (size_t)z * hq * s_q * 4 : 0;
+}
+
+struct SplitPlan {
+  int n_split, split_tiles;
+};
+
+// Chooses the key splits of one call from the tile counts of its query blocks
+// (without documents, which only shorten a block's tile range). Each candidate
+// is scored by simulating the hardware's in-order dispatch of the grid onto
+// the compute units (a unit takes the next workgroup when it frees up), in
+// units of one 64-key tile of one workgroup, plus the merge's memory traffic
+// in the same units; splitting must save at least 15%.
+SplitPlan plan_splits(int64_t s_q, int64_t q_off, int64_t k_off, int64_t s_kv, int causal, int hq,
+                      int hkv, int d, size_t room) {
+  const int cap = split_cap(s_q, hq, hkv);
+  if (cap <= 1 || s_q < 1) return {1, 0};
+  const int qrows = qrows_for(hq, hkv);
+  const int nqb = (int)((s_q + qrows - 1) / qrows);
+  const int heads = (int)(grid_size(s_q, hq, hkv) / nqb);
+  std::vector<int> nt(nqb);
+  int max_nt = 0;
+  for (int b = 0; b < nqb; ++b) {
+    const int64_t last = std::min<int64_t>((int64_t)(b + 1) * qrows, s_q) - 1;
+    const int64_t hi = causal ? std::min(q_off + last - k_off, s_kv - 1) : s_kv - 1;
+    nt[b] = hi >= 0 ? (int)(hi / BN + 1) : 0;
+    max_nt = std::max(max_nt, nt[b]);
+  }
+  // one tile of one workgroup is 8 * 32 rows * 64 keys * 4d FLOP; at about
+  // 4.3 TFLOP/s per compute unit and 5 TB/s that is worth d * 76 KB of traffic
+  const double bytes_per_tile = 76.0e3 * d;
+  double base = 0, best_cost = 0;
+  SplitPlan best{1, 0};
+  for (int z = 1; z <= cap; ++z) {
+    const int c = (max_nt + z - 1) / z;
+    if (z > 1 && (c < kMinSplitTiles || split_bytes(z, s_q, hq, d) > room)) break;
+    std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
+    for (int i = 0; i < kCUs; ++i) cu.push(0.0);
+    double makespan = 0, items = 0;
+    for (int y = 0; y < heads; ++y)
+      for (int b = nqb - 1; b >= 0; --b)
+        for (int k = 0; k < z; ++k) {
+          const int len = z > 1 ? std::min(nt[b] - k * c, c) : nt[b];
+          if (len <= 0) continue;
+          const double f = cu.top() + len + 0.5;  // 0.5: prologue and epilogue
+          cu.pop();
+          cu.push(f);
+          makespan = std::max(makespan, f);
+          items += 1;
+        }
+    double cost = makespan;
+    if (z > 1)  // partial O written and read back, final O written, launch
+      cost += 2.0 + (items * qrows * hg_for(hq / hkv) * d * 8.0 + (double)s_q * hq * d * 2) /
+                        bytes_per_tile;
+    if (z == 1) {
+      base = best_cost = cost;
+    } else if (cost < 0.85 * base && cost < best_cost) {
+      best_cost = cost;
+      best = {z, c};
+    }
+  }
+  return best;
 }
 
 template <int D, int HG>
@@ -363,7 +524,7 @@ int launch_fwd(const FwdParams& p, int g, int hkv, hipStream_t stream) {
   constexpr int QROWS = 32 * (8 / HG);
   FwdParams pr = p;
   pr.n_qblocks = (p.m.s_q + QROWS - 1) / QROWS;
-  dim3 grid((unsigned)pr.n_qblocks, (unsigned)(hkv * (g / HG)));
+  dim3 grid((unsigned)(pr.n_qblocks * pr.n_split), (unsigned)(hkv * (g / HG)));
   TraceScope ts("attn_fwd_bf16", stream);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, HG>), grid, dim3(512), 0, stream, pr);
   return hipGetLastError() == hipSuccess ? USP_OK : USP_ERR_HIP;
@@ -376,30 +537,76 @@ int fwd_dispatch(const FwdParams& p, int g, int hkv, hipStream_t stream) {
   return launch_fwd<D, 1>(p, g, hkv, stream);
 }
 
+int split_merge_launch(const float* part, const float* plse, int64_t o_split, int64_t lse_split,
+                       int nz, void* o, float* lse, int64_t s_q, int hq, int d, int out_f32,
+                       hipStream_t stream) {
+  const int n = (int)(s_q * hq * (d / 8));
+  const dim3 grid((unsigned)((n + 255) / 256));
+  TraceScope ts("attn_fwd_merge", stream);
+  const FastDiv fd = FastDiv::make((uint32_t)hq);
+  if (d == 64)
+    hipLaunchKernelGGL((split_merge_kernel<64>), grid, dim3(256), 0, stream, part, plse, o_split,
+                       lse_split, nz, o, lse, (int)s_q, fd, n, out_f32);
+  else
+    hipLaunchKernelGGL((split_merge_kernel<128>), grid, dim3(256), 0, stream, part, plse,
+                       o_split, lse_split, nz, o, lse, (int)s_q, fd, n, out_f32);
+  return hipGetLastError() == hipSuccess ? USP_OK : USP_ERR_HIP;
+}
+
 }  // namespace
 
-size_t attn_fwd_bf16_workspace(int64_t s_k, int, int hkv, int d) {
-  return (size_t)hkv * d * kmajor_len(s_k) * 2;
+// The V copy, then room for the key splits of a call of s_k query rows.
+size_t attn_fwd_bf16_workspace(int64_t s_k, int hq, int hkv, int d) {
+  return vcopy_bytes(s_k, hkv, d) + split_bytes(split_cap(s_k, hq, hkv), s_k, hq, d);
+}
+
+size_t attn_fwd_bf16_min_workspace(int64_t s_k, int hkv, int d) { return vcopy_bytes(s_k, hkv, d); }
+
+int attn_fwd_bf16_splits(const AttnArgs& a) {
+  const size_t v = vcopy_bytes(a.s_k, a.hkv, a.d);
+  const size_t room = a.workspace_bytes > v ? a.workspace_bytes - v : 0;
+  return plan_splits(a.s_q, a.q_off, a.k_off, a.s_kv, a.causal, a.hq, a.hkv, a.d, room).n_split;
 }
 
 int attn_fwd_bf16(const AttnArgs& a) {
   const int64_t s_t = kmajor_len(a.s_k);
   int rc = kmajor_launch(a.v, a.workspace, a.s_k, a.hkv, a.d, s_t, a.stream, "attn_fwd_kmajor_v");
   if (rc != USP_OK) return rc;
+  const size_t v = vcopy_bytes(a.s_k, a.hkv, a.d);
+  const size_t room = a.workspace_bytes > v ? a.workspace_bytes - v : 0;
+  const SplitPlan sp =
+      plan_splits(a.s_q, a.q_off, a.k_off, a.s_kv, a.causal, a.hq, a.hkv, a.d, room);
   FwdParams p{};
   p.q = static_cast<const __bf16*>(a.q);
   p.k = static_cast<const __bf16*>(a.k);
   p.vt = static_cast<const __bf16*>(a.workspace);
-  p.o = a.out_f32 ? nullptr : static_cast<__bf16*>(a.o_out);
-  p.o32 = a.out_f32 ? static_cast<float*>(a.o_out) : nullptr;
   p.lse = a.lse_out;
   p.m = mask_geom(a);
   p.s_t = s_t;
   p.hq = a.hq;
   p.hkv = a.hkv;
   p.scale_log2 = a.scale * kLog2e;
+  p.n_split = sp.n_split;
+  p.split_tiles = sp.split_tiles;
+  float* part = nullptr;
+  float* plse = nullptr;
+  if (sp.n_split > 1) {
+    part = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + v);
+    plse = reinterpret_cast<float*>(reinterpret_cast<char*>(part) +
+                                    align256((size_t)sp.n_split * a.s_q * a.hq * a.d * 4));
+    p.o32 = part;
+    p.lse = plse;
+    p.o_split = a.s_q * a.hq * a.d;
+    p.lse_split = a.s_q * a.hq;
+  } else {
+    p.o = a.out_f32 ? nullptr : static_cast<__bf16*>(a.o_out);
+    p.o32 = a.out_f32 ? static_cast<float*>(a.o_out) : nullptr;
+  }
   const int g = a.hq / a.hkv;
-  return a.d == 64 ? fwd_dispatch<64>(p, g, a.hkv, a.stream) : fwd_dispatch<128>(p, g, a.hkv, a.stream);
+  rc = a.d == 64 ? fwd_dispatch<64>(p, g, a.hkv, a.stream) : fwd_dispatch<128>(p, g, a.hkv, a.stream);
+  if (rc != USP_OK || sp.n_split <= 1) return rc;
+  return split_merge_launch(part, plse, p.o_split, p.lse_split, sp.n_split, a.o_out, a.lse_out,
+                            a.s_q, a.hq, a.d, a.out_f32, a.stream);
 }
 
 }  // namespace usp

@@ -106,11 +106,13 @@ int fwd_checked(const void* q, const void* k, const void* v, void* o, float* lse
   const size_t qb = (size_t)s_q * hq * d * es, kb = (size_t)s_k * hkv * d * es;
   const size_t ob = (size_t)s_q * hq * d * elem_bytes(o_dtype);
   const size_t lb = (size_t)s_q * hq * sizeof(float);
-  const size_t need = usp_attn_fwd_workspace_bytes(s_k, hq, hkv, d, dtype);
+  // bf16: the key-major V copy is required; room beyond it (as much as
+  // usp_attn_fwd_workspace_bytes) lets a short call split its keys
+  const size_t need = dtype == USP_BF16 ? usp::attn_fwd_bf16_min_workspace(s_k, hkv, d) : 0;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return USP_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return USP_ERR_INVALID;
   const Span ins[] = {{q, qb}, {k, kb}, {v, kb}};
-  const Span outs[] = {{o, ob}, {lse, lb}, {workspace, need}};
+  const Span outs[] = {{o, ob}, {lse, lb}, {workspace, need > 0 ? workspace_bytes : 0}};
   for (const Span& a : outs) {
     for (const Span& b : ins)
       if (overlap(a, b)) return USP_ERR_INVALID;
@@ -120,7 +122,7 @@ int fwd_checked(const void* q, const void* k, const void* v, void* o, float* lse
   usp::AttnArgs a = interval_args(s_q, q_off, s_k, k_off, s_k_valid, cu, n_docs, hq, hkv, d,
                                   scale, causal, stream);
   a.q = q; a.k = k; a.v = v;
-  a.o_out = o; a.lse_out = lse; a.workspace = workspace;
+  a.o_out = o; a.lse_out = lse; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
   a.out_f32 = o_dtype == USP_FP32;
   return dtype == USP_BF16 ? usp::attn_fwd_bf16(a) : usp::attn_fwd_f32(a);
 }
@@ -266,6 +268,19 @@ int usp_attn_fwd_interval(const void* q, const void* k, const void* v, void* o, 
   return fwd_checked(q, k, v, o, lse, workspace, workspace_bytes, s_q, q_off, s_k, k_off,
                      s_k_valid, cu_seqlens, n_docs, hq, hkv, d, softmax_scale, causal, dtype,
                      o_dtype, stream);
+}
+
+int usp_attn_fwd_num_splits(int64_t s_q, int64_t q_off, int64_t s_k, int64_t k_off,
+                            int64_t s_k_valid, int hq, int hkv, int d, int causal, int dtype,
+                            size_t workspace_bytes) {
+  const int rc = check_interval(s_q, q_off, s_k, k_off, s_k_valid, nullptr, 0, hq, hkv, d, 1.0f,
+                                causal, dtype);
+  if (rc != USP_OK) return rc;
+  if (dtype != USP_BF16) return 1;
+  usp::AttnArgs a = interval_args(s_q, q_off, s_k, k_off, s_k_valid, nullptr, 0, hq, hkv, d, 1.0f,
+                                  causal, nullptr);
+  a.workspace_bytes = workspace_bytes;
+  return usp::attn_fwd_bf16_splits(a);
 }
 
 int usp_attn_bwd_interval(const void* q, const void* k, const void* v, const void* o,

@@ -63,6 +63,7 @@ struct AttnArgs {
   void* dk;
   void* dv;
   void* workspace;
+  size_t workspace_bytes;
   int64_t s_q, s_k, s_kv, q_off, k_off, lim;
   const int32_t* cu;
   int n_docs;
@@ -106,8 +107,11 @@ int kmajor_launch(const void* src, void* dst, int64_t s_pad, int heads, int d, i
                   hipStream_t stream, const char* trace_name);
 
 size_t attn_fwd_bf16_workspace(int64_t s_k, int hq, int hkv, int d);
+size_t attn_fwd_bf16_min_workspace(int64_t s_k, int hkv, int d);  // the V copy alone
 size_t attn_bwd_bf16_workspace(int64_t s_q, int64_t s_k, int hq, int hkv, int d);
 int attn_fwd_bf16(const AttnArgs& a);
+// Key splits the bf16 forward runs for these arguments (1: a single pass).
+int attn_fwd_bf16_splits(const AttnArgs& a);
 int attn_bwd_bf16(const AttnArgs& a);
 int attn_fwd_f32(const AttnArgs& a);
 int attn_bwd_f32(const AttnArgs& a);
