@@ -454,7 +454,7 @@ def main():
 
     fwd_ms = kms("attn_fwd_kmajor_v", "attn_fwd_bf16", "attn_fwd_merge")
     bwd_ms = kms("attn_bwd_kmajor", "attn_bwd_rowdot_bf16", "attn_bwd_dkdv_bf16",
-                 "attn_bwd_dkdv_reduce", "attn_bwd_dq_bf16")
+                 "attn_bwd_dkdv_reduce", "attn_bwd_dq_bf16", "attn_bwd_dq_reduce")
     perm_ms = kms("pack_seq2head", "unpack_head2seq")
 
     # ---- dominant kernel roofline
@@ -543,6 +543,8 @@ def main():
         # key splits of the forward (1: one pass; more on short sequences)
         "attn_fwd_key_splits": usp.usp_attn_fwd_num_splits(
             s_pad, s_pad, hq, hkv, d, 0, s_k_valid=w.s, workspace_bytes=ws_f.numel()),
+        "attn_bwd_dq_key_splits": usp.usp_attn_bwd_num_splits(
+            s_pad, s_pad, hq, hkv, d, 0, s_k_valid=w.s, workspace_bytes=ws_b.numel()),
         "attn_fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 1),
         "attn_fwd_bwd_tflops": round((f_fwd + f_bwd) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 1),
         "attn_fwd_frac_of_peak": round(f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),

@@ -135,7 +135,13 @@ int usp_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 /* Workspace bytes usp_attn_bwd needs for these sizes: per (query head, row)
  * fp32 D and LSE values and, for bf16 on short sequences (fewer than 512
  * blocks of 128 keys over all KV heads), fp32 partial dK and dV per row
- * chunk; deterministic in the sizes. */
+ * chunk; deterministic in the sizes. That much is required. For bf16 the
+ * size returned also holds room for up to 8 key splits of dQ when the dQ grid
+ * has fewer than 1024 workgroups (fp32 partial dQ of every row, summed in a
+ * fixed order afterwards; see usp_attn_bwd_num_splits): about 134 MB at
+ * s_pad = 8192 with 4 query heads and d = 128. With less room the call splits
+ * less (one pass with none), same results up to rounding. The whole
+ * workspace_bytes range must not overlap the other arguments. */
 size_t usp_attn_bwd_workspace_bytes(int64_t s_pad, int hq, int hkv, int d, int dtype);
 
 /*
@@ -211,6 +217,21 @@ int usp_attn_fwd_interval(const void* q, const void* k, const void* v, void* o, 
  * these sizes (USP_ERR_INVALID, USP_ERR_UNSUPPORTED).
  */
 int usp_attn_fwd_num_splits(int64_t s_q, int64_t q_off, int64_t s_k, int64_t k_off,
+                            int64_t s_k_valid, int hq, int hkv, int d, int causal, int dtype,
+                            size_t workspace_bytes);
+
+/*
+ * Number of key splits the dQ kernel of usp_attn_bwd / usp_attn_bwd_interval
+ * runs for these arguments with a workspace of workspace_bytes bytes (1: a
+ * single pass). With n > 1 each block of query rows has its key tiles cut
+ * into n consecutive ranges run by separate workgroups, each writing an fp32
+ * partial dQ into the workspace; a reduction kernel adds them in split order
+ * (deterministic) and writes dq (or adds to it when accumulating). dK and dV
+ * are unaffected. Like usp_attn_fwd_num_splits, host-only and independent of
+ * cu_seqlens' contents and the data. Returns the count or the error the call
+ * would return for these sizes.
+ */
+int usp_attn_bwd_num_splits(int64_t s_q, int64_t q_off, int64_t s_k, int64_t k_off,
                             int64_t s_k_valid, int hq, int hkv, int d, int causal, int dtype,
                             size_t workspace_bytes);
 

@@ -132,6 +132,9 @@ def test_attention_argument_errors(L, f):
     assert f(L, ws=(3 << 30) + 8) == INVALID            # misaligned workspace
     if f is fwd:  # the forward needs its V copy (128 x 256 x 2 bytes) at least
         assert f(L, ws_bytes=128 * 256 * 2 - 16) == WORKSPACE
+    else:  # the backward its D and LSE rows (two 4 x 256 fp32 arrays) and chunk partials
+        req = L.usp_attn_bwd_workspace_bytes(256, 4, 1, 128, BF16) - dq_room(256, 4, 1, 128)
+        assert f(L, ws_bytes=req - 16) == WORKSPACE
 
 
 def test_attention_null_and_alias(L):
@@ -235,10 +238,25 @@ def dkdv_chunks(s_q, s_k, hkv):
     return max(1, min(-(-1024 // items), -(-s_q // 64), 16))
 
 
+def dq_split_cap(s_q, hq, hkv):
+    """Most dQ key splits: 1 when the dQ grid (workgroups of HG query heads x
+    4/HG blocks of 32 rows) has 1024 workgroups or more, else enough for
+    about 2048, at most 8."""
+    g = hq // hkv
+    hg = 4 if g % 4 == 0 else 2 if g % 2 == 0 else 1
+    wgs = -(-s_q // (32 * (4 // hg))) * hkv * (g // hg)
+    return 1 if wgs >= 1024 else min(8, -(-2048 // wgs))
+
+
+def dq_room(s_q, hq, hkv, d):
+    z = dq_split_cap(s_q, hq, hkv)
+    return z * s_q * hq * d * 4 if z > 1 else 0
+
+
 def test_workspace_sizes(L):
     for s in (1, 100, 128, 129, 120000, 131072):
         f = L.usp_attn_fwd_workspace_bytes(s, 4, 1, 128, BF16)
-        b = L.usp_attn_bwd_workspace_bytes(s, 4, 1, 128, BF16)
+        b = L.usp_attn_bwd_workspace_bytes(s, 4, 1, 128, BF16) - dq_room(s, 4, 1, 128)
         assert f >= 128 * s * 2 and f % 16 == 0
         # fp32 partial dK and dV per row chunk when the rows are split
         n = dkdv_chunks(s, s, 1)
@@ -254,6 +272,7 @@ def test_workspace_sizes(L):
     for s_q, s_k in ((100, 1000), (1000, 100), (512, 512), (30000, 30000)):
         for hkv, d in ((1, 128), (4, 64)):
             b = L.usp_attn_bwd_interval_workspace_bytes(s_q, s_k, 4 * hkv, hkv, d, BF16)
+            b -= dq_room(s_q, 4 * hkv, hkv, d)
             n = dkdv_chunks(s_q, s_k, hkv)
             part = 2 * n * s_k * hkv * d * 4 if n > 1 else 0
             assert 2 * 4 * hkv * s_q * 4 <= b - part < 2 * 4 * hkv * (s_q + 128) * 4 + 512
@@ -301,6 +320,21 @@ def test_fwd_workspace_and_key_splits(L):
     assert split(15000, 105000, 120000, 0, 120000, 4, 1, 128, 1, BF16) == 1
     # fewer than 8 tiles per split: one pass
     assert split(300, 0, 300, 0, 300, 4, 1, 128, 1, BF16) == 1
+    # dQ: the same for the backward's workspace and its dQ key splits
+    for s, hq, hkv, d in ((8192, 4, 1, 128), (16384, 4, 1, 128), (32768, 4, 1, 128),
+                          (1000, 8, 2, 64), (120000, 4, 1, 128), (64, 4, 1, 128)):
+        wb = L.usp_attn_bwd_workspace_bytes(s, hq, hkv, d, BF16)
+        req = wb - dq_room(s, hq, hkv, d)
+        for causal in (0, 1):
+            n = L.usp_attn_bwd_num_splits(s, 0, s, 0, s, hq, hkv, d, causal, BF16, wb)
+            assert 1 <= n <= dq_split_cap(s, hq, hkv)
+            assert L.usp_attn_bwd_num_splits(s, 0, s, 0, s, hq, hkv, d, causal, BF16, req) == 1
+            assert L.usp_attn_bwd_num_splits(s, 0, s, 0, s, hq, hkv, d, causal, FP32, wb) == 1
+    bsplit = lambda s, hq, hkv, d: L.usp_attn_bwd_num_splits(
+        s, 0, s, 0, s, hq, hkv, d, 1, BF16, L.usp_attn_bwd_workspace_bytes(s, hq, hkv, d, BF16))
+    assert bsplit(8192, 4, 1, 128) > 1 and bsplit(16384, 4, 1, 128) > 1
+    assert bsplit(32768, 4, 1, 128) == 1 and bsplit(120000, 4, 1, 128) == 1
+    assert L.usp_attn_bwd_num_splits(0, 0, 8, 0, 8, 4, 1, 128, 1, BF16, 1 << 30) == -1
     # argument errors as in the interval forward
     assert L.usp_attn_fwd_num_splits(0, 0, 8, 0, 8, 4, 1, 128, 1, BF16, 1 << 30) == -1
     assert L.usp_attn_fwd_num_splits(8, 0, 8, 0, 8, 4, 1, 96, 1, BF16, 1 << 30) == -2

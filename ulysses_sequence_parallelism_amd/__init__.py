@@ -31,6 +31,7 @@ __all__ = [
     "usp_attn_bwd",
     "usp_attn_fwd_interval",
     "usp_attn_fwd_num_splits",
+    "usp_attn_bwd_num_splits",
     "usp_attn_merge",
     "usp_attn_bwd_interval_workspace_bytes",
     "usp_attn_bwd_interval",
@@ -98,6 +99,8 @@ def lib() -> ctypes.CDLL:
                                             vp, i32, i32, i32, i32, f32, i32, i32, i32, vp]
         L.usp_attn_fwd_num_splits.restype = i32
         L.usp_attn_fwd_num_splits.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32, i32, i32, sz]
+        L.usp_attn_bwd_num_splits.restype = i32
+        L.usp_attn_bwd_num_splits.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32, i32, i32, sz]
         L.usp_attn_merge.restype = i32
         L.usp_attn_merge.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, vp]
         L.usp_attn_bwd_interval_workspace_bytes.restype = sz
@@ -216,6 +219,20 @@ def usp_attn_fwd_num_splits(s_q: int, s_k: int, hq: int, hkv: int, d: int, dtype
                                       hq, hkv, d, int(causal), dtype, workspace_bytes)
     if n < 1:
         raise UspError("usp_attn_fwd_num_splits", n)
+    return n
+
+
+def usp_attn_bwd_num_splits(s_q: int, s_k: int, hq: int, hkv: int, d: int, dtype: int,
+                            causal: bool = True, q_off: int = 0, k_off: int = 0,
+                            s_k_valid: int | None = None, workspace_bytes: int | None = None) -> int:
+    """Key splits the dQ kernel runs for these sizes (1: one pass). The default
+    workspace is the one the binding allocates for the backward."""
+    if workspace_bytes is None:
+        workspace_bytes = usp_attn_bwd_interval_workspace_bytes(s_q, s_k, hq, hkv, d, dtype)
+    n = lib().usp_attn_bwd_num_splits(s_q, q_off, s_k, k_off, s_k if s_k_valid is None else s_k_valid,
+                                      hq, hkv, d, int(causal), dtype, workspace_bytes)
+    if n < 1:
+        raise UspError("usp_attn_bwd_num_splits", n)
     return n
 
 

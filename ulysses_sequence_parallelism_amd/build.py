@@ -34,7 +34,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 SOURCES = ["capi.hip", "trace.hip", "permute.hip", "kmajor.hip", "attn_f32.hip", "attn_fwd_bf16.hip",
-           "attn_bwd_bf16.hip", "merge.hip"]
+           "attn_bwd_bf16.hip", "merge.hip", "splits.hip"]
 # The matrix-core attention kernels never produce a NaN (masked scores are
 # -inf, and every difference of two infinities is guarded), so they are built
 # without NaN semantics: the row max then compiles to v_max3_f32 directly

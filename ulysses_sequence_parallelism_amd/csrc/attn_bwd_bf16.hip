@@ -33,6 +33,7 @@
 //   * Tiles go straight from global memory into double-buffered, swizzled LDS
 //     slots; masks are applied only on boundary tiles, and the causal
 //     triangle is launched heaviest-first.
+#include <algorithm>
 #include <type_traits>
 
 #include "usp_common.h"
@@ -94,6 +95,13 @@ struct BwdParams {
   // ([2][n_ch][s_k][hkv][D], dV first), summed afterwards in chunk order
   int n_kb, n_ch, cht;
   float* part;
+  // dQ key splits: grid x = n_blocks query blocks x dq_split; with dq_split > 1
+  // split z of a block takes tiles [z, z + 1) * dq_tiles of its key range and
+  // writes its scaled fp32 partial dQ to dq_part + z * dq_stride, summed
+  // afterwards in split order
+  int dq_split, dq_tiles;
+  float* dq_part;
+  int64_t dq_stride;
   int grad_f32, accum;  // fp32 gradients; add to the existing contents
   float scale, scale_log2;
 };
@@ -527,7 +535,9 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
   const int chunks = g / HG;
   const int kvh = blockIdx.y / chunks, hc = blockIdx.y % chunks;
   const int head = kvh * g + hc * HG + (w % HG);
-  const int qb = pr.n_blocks - 1 - (int)blockIdx.x;
+  // heaviest query block first; its key splits follow one another
+  const int qb = pr.n_blocks - 1 - (int)blockIdx.x / pr.dq_split;
+  const int zs = (int)blockIdx.x % pr.dq_split;
   const int q0 = qb * QROWS;
   const int q1 = min(q0 + QROWS, s_q);
   const int wq0 = q0 + (w / HG) * 32;
@@ -538,8 +548,15 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
   const KeyRange kr = row_keys(pr.m, qc);
   const int lo = kr.lo, hi = kr.hi;
   const KeyRange kfirst = row_keys(pr.m, q0), klast = row_keys(pr.m, q1 - 1);
-  const int kmin = kfirst.lo, kmax = klast.hi;
+  // workgroup key range; with key splits, the part of it in this split's
+  // tiles (counted from the tile holding the first key)
+  const int t_split = (kfirst.lo / BN + zs * pr.dq_tiles) * BN;
+  const int kmin = pr.dq_split > 1 ? max(kfirst.lo, t_split) : kfirst.lo;
+  const int kmax = pr.dq_split > 1 ? min(klast.hi, t_split + pr.dq_tiles * BN - 1) : klast.hi;
   const int free_lo = klast.lo, free_hi = kfirst.hi;
+  const int tstart = (kmin / BN) * BN;
+  const int nt = kmax >= kmin ? (kmax - tstart) / BN + 1 : 0;
+  if (pr.dq_split > 1 && nt == 0) return;  // no keys here: the sum skips this split
   const int wkmin = row_keys(pr.m, min(wq0, s_q - 1)).lo;
   const int wkmax = row_keys(pr.m, min(wq0 + 31, s_q - 1)).hi;
 
@@ -560,9 +577,6 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
   f32x16 dqa[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) dqa[b] = f32x16{};
-
-  const int tstart = (kmin / BN) * BN;
-  const int nt = kmax >= kmin ? (kmax - tstart) / BN + 1 : 0;
 
   // A part is one 1 KiB wave-load (RPP keys of K or V); wave w brings K and V
   // parts PPW w .. +PPW-1 as inline-asm direct loads (see lds_dma16): a
@@ -704,9 +718,45 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
     if (it + 1 < nt) step(it + 1, std::integral_constant<int, 1>{});
   }
 
-  if (row_ok)
-    store_rows<DB>(pr.dq, ((int64_t)qi * pr.hq + head) * D + hl * 4, dqa, pr.scale, pr.grad_f32,
-               pr.accum);
+  if (row_ok) {
+    const bool split = pr.dq_split > 1;
+    store_rows<DB>(split ? static_cast<void*>(pr.dq_part + zs * pr.dq_stride) : pr.dq,
+                   ((int64_t)qi * pr.hq + head) * D + hl * 4, dqa, pr.scale,
+                   split ? 1 : pr.grad_f32, split ? 0 : pr.accum);
+  }
+}
+
+// dQ from the key splits' partial sums, added in split order (the result does
+// not depend on scheduling). Split z of a query block holds keys only when the
+// block has more than z * tiles_per_split key tiles, found from the mask
+// geometry exactly as the dQ kernel finds them; the other splits wrote nothing
+// and are not read (a block with no keys gets dQ = 0). One thread per 4
+// values; a row has row4 groups of 4 values.
+__global__ __launch_bounds__(256) void dq_reduce_kernel(const float* __restrict__ part,
+                                                        int64_t stride, int nz,
+                                                        int tiles_per_split, int key_tile,
+                                                        MaskGeom m, int qrows, uint32_t row4,
+                                                        void* dq, uint32_t n4, int f32, int accum) {
+  const uint32_t i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const int row = (int)(i / row4);
+  const int q0 = row / qrows * qrows;
+  const int q1 = min(q0 + qrows, m.s_q);
+  const KeyRange kf = row_keys(m, q0), kl = row_keys(m, q1 - 1);
+  const int tstart = kf.lo / key_tile * key_tile;
+  const int nt = kl.hi >= kf.lo ? (kl.hi - tstart) / key_tile + 1 : 0;
+  const int nzr = min(nz, (nt + tiles_per_split - 1) / tiles_per_split);
+  const f32x4* src = reinterpret_cast<const f32x4*>(part) + i;
+  f32x4 acc = {};
+  for (int z = 0; z < nzr; ++z) acc += src[z * (stride / 4)];
+  if (f32) {
+    f32x4* o = reinterpret_cast<f32x4*>(dq) + i;
+    if (accum) acc += *o;
+    *o = acc;
+  } else {
+    const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    reinterpret_cast<u32x2*>(dq)[i] = v;
+  }
 }
 
 constexpr int kDqKeys = 32;      // keys per dQ tile
@@ -728,14 +778,69 @@ int dkdv_row_chunks(int64_t s_q, int64_t s_k, int hkv) {
   return n > 1 ? (int)n : 1;
 }
 
+int hg_for(int g) { return g % 4 == 0 ? 4 : g % 2 == 0 ? 2 : 1; }
+int dq_qrows(int hq, int hkv) { return 32 * (4 / hg_for(hq / hkv)); }
+
+// dQ key splits pay off only while the unsplit grid is short of a few rounds
+// of workgroups on the 512 resident slots (two 4-wave workgroups per compute
+// unit).
+constexpr int kDqSlots = 512;
+constexpr int kDqMaxSplits = 8;
+int dq_split_cap(int64_t s_q, int hq, int hkv) {
+  const int g = hq / hkv;
+  const int64_t wgs = (s_q + dq_qrows(hq, hkv) - 1) / dq_qrows(hq, hkv) * hkv * (g / hg_for(g));
+  if (wgs >= 2 * kDqSlots) return 1;
+  return (int)std::min<int64_t>(kDqMaxSplits, (4 * kDqSlots + wgs - 1) / wgs);
+}
+
+size_t dq_split_bytes(int z, int64_t s_q, int hq, int d) {
+  return z > 1 ? (size_t)z * s_q * hq * d * 4 : 0;
+}
+
+// The dQ key splits of a call with `room` workspace bytes for the partials.
+// One 32-key tile of a 4-wave workgroup takes about 1.3 us at d = 128 with two
+// workgroups per compute unit; at 5 TB/s that is d x 52 KB of traffic.
+SplitPlan plan_dq(int64_t s_q, int64_t q_off, int64_t k_off, int64_t s_kv, int causal, int hq,
+                  int hkv, int d, size_t room) {
+  int cap = dq_split_cap(s_q, hq, hkv);
+  while (cap > 1 && dq_split_bytes(cap, s_q, hq, d) > room) --cap;
+  SplitProblem sp{};
+  sp.s_q = s_q;
+  sp.q_off = q_off;
+  sp.k_off = k_off;
+  sp.s_kv = s_kv;
+  sp.causal = causal;
+  sp.qrows = dq_qrows(hq, hkv);
+  sp.heads = hkv * (hq / hkv / hg_for(hq / hkv));
+  sp.key_tile = kDqKeys;
+  sp.slots = kDqSlots;
+  sp.cap = cap;
+  sp.min_tiles = 16;
+  // each (block, split) partial is written and read back; dQ written once
+  sp.item_bytes = (double)sp.qrows * hg_for(hq / hkv) * d * 8;
+  sp.fixed_bytes = (double)s_q * hq * d * 2;
+  sp.tile_bytes = 52.0e3 * d;
+  return plan_key_splits(sp);
+}
+
 template <int D, int HG>
-int launch_dq(const BwdParams& p, int g, hipStream_t stream) {
+int launch_dq(const BwdParams& p, int g, const AttnArgs& a) {
   constexpr int QROWS = 32 * (4 / HG);
   BwdParams pr = p;
   pr.n_blocks = (p.m.s_q + QROWS - 1) / QROWS;
-  dim3 grid((unsigned)pr.n_blocks, (unsigned)(p.hkv * (g / HG)));
-  TraceScope ts("attn_bwd_dq_bf16", stream);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, HG, kDqKeys>), grid, dim3(256), 0, stream, pr);
+  dim3 grid((unsigned)(pr.n_blocks * pr.dq_split), (unsigned)(p.hkv * (g / HG)));
+  {
+    TraceScope ts("attn_bwd_dq_bf16", a.stream);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, HG, kDqKeys>), grid, dim3(256), 0, a.stream, pr);
+    if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
+  }
+  if (pr.dq_split <= 1) return USP_OK;
+  const uint32_t n4 = (uint32_t)(a.s_q * a.hq * D / 4);
+  TraceScope ts("attn_bwd_dq_reduce", a.stream);
+  hipLaunchKernelGGL(dq_reduce_kernel, dim3((n4 + 255) / 256), dim3(256), 0, a.stream,
+                     static_cast<const float*>(pr.dq_part), pr.dq_stride, pr.dq_split, pr.dq_tiles,
+                     kDqKeys, pr.m, QROWS, (uint32_t)(a.hq * D / 4), a.dq, n4, a.out_f32,
+                     a.accumulate);
   return hipGetLastError() == hipSuccess ? USP_OK : USP_ERR_HIP;
 }
 
@@ -776,21 +881,39 @@ int bwd_launch(const BwdParams& p, const AttnArgs& a, float* dd, float* lse2, fl
     }
   }
   const int g = a.hq / a.hkv;
-  if (g % 4 == 0) return launch_dq<D, 4>(p, g, a.stream);
-  if (g % 2 == 0) return launch_dq<D, 2>(p, g, a.stream);
-  return launch_dq<D, 1>(p, g, a.stream);
+  if (g % 4 == 0) return launch_dq<D, 4>(p, g, a);
+  if (g % 2 == 0) return launch_dq<D, 2>(p, g, a);
+  return launch_dq<D, 1>(p, g, a);
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-}  // namespace
-
-size_t attn_bwd_bf16_workspace(int64_t s_q, int64_t s_k, int hq, int hkv, int d) {
-  // D and LSE*log2(e) per query row and head, then the dK/dV row-chunk partials
+// Required part of the workspace: D and LSE*log2(e) per query row and head,
+// then the dK/dV row-chunk partials (256-byte aligned).
+size_t bwd_required(int64_t s_q, int64_t s_k, int hq, int hkv, int d) {
   const size_t rows = align256((size_t)hq * (size_t)kmajor_len(s_q) * 4) * 2;
   const int n_ch = dkdv_row_chunks(s_q, s_k, hkv);
-  return rows + (n_ch > 1 ? (size_t)2 * n_ch * (size_t)s_k * hkv * d * 4 : 0);
+  return rows + align256(n_ch > 1 ? (size_t)2 * n_ch * (size_t)s_k * hkv * d * 4 : 0);
 }
+
+SplitPlan plan_dq_for(const AttnArgs& a) {
+  const size_t req = bwd_required(a.s_q, a.s_k, a.hq, a.hkv, a.d);
+  const size_t room = a.workspace_bytes > req ? a.workspace_bytes - req : 0;
+  return plan_dq(a.s_q, a.q_off, a.k_off, a.s_kv, a.causal, a.hq, a.hkv, a.d, room);
+}
+
+}  // namespace
+
+// The required part, then room for the dQ key splits of s_q rows.
+size_t attn_bwd_bf16_workspace(int64_t s_q, int64_t s_k, int hq, int hkv, int d) {
+  return bwd_required(s_q, s_k, hq, hkv, d) + dq_split_bytes(dq_split_cap(s_q, hq, hkv), s_q, hq, d);
+}
+
+size_t attn_bwd_bf16_min_workspace(int64_t s_q, int64_t s_k, int hq, int hkv, int d) {
+  return bwd_required(s_q, s_k, hq, hkv, d);
+}
+
+int attn_bwd_bf16_dq_splits(const AttnArgs& a) { return plan_dq_for(a).n_split; }
 
 int attn_bwd_bf16(const AttnArgs& a) {
   const int64_t s_tq = kmajor_len(a.s_q);
@@ -817,6 +940,11 @@ int attn_bwd_bf16(const AttnArgs& a) {
   p.accum = a.accumulate;
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
+  const SplitPlan dp = plan_dq_for(a);
+  p.dq_split = dp.n_split;
+  p.dq_tiles = dp.split_tiles;
+  p.dq_part = reinterpret_cast<float*>(ws + bwd_required(a.s_q, a.s_k, a.hq, a.hkv, a.d));
+  p.dq_stride = a.s_q * a.hq * a.d;
   return a.d == 64 ? bwd_launch<64>(p, a, dd, lse2, part) : bwd_launch<128>(p, a, dd, lse2, part);
 }
 

@@ -54,9 +54,7 @@
 //   * Workgroups are launched heaviest-first (last query block first) so the
 //     causal triangle's long rows start early and the tail is short.
 #include <algorithm>
-#include <queue>
 #include <type_traits>
-#include <vector>
 
 #include "usp_common.h"
 #include "usp_internal.h"
@@ -458,65 +456,30 @@ size_t split_bytes(int z, int64_t s_q, int hq, int d) {
   return z > 1 ? align256((size_t)z * s_q * hq * d * 4) + (size_t)z * hq * s_q * 4 : 0;
 }
 
-struct SplitPlan {
-  int n_split, split_tiles;
-};
-
-// Chooses the key splits of one call from the tile counts of its query blocks
-// (without documents, which only shorten a block's tile range). Each candidate
-// is scored by simulating the hardware's in-order dispatch of the grid onto
-// the compute units (a unit takes the next workgroup when it frees up), in
-// units of one 64-key tile of one workgroup, plus the merge's memory traffic
-// in the same units; splitting must save at least 15%.
+// Key splits of one call, within the workspace room for the partials. One
+// tile of one 8-wave workgroup is 8 x 32 rows x 64 keys x 4d FLOP: at about
+// 4.3 TFLOP/s per compute unit and 5 TB/s, d x 76 KB of traffic.
 SplitPlan plan_splits(int64_t s_q, int64_t q_off, int64_t k_off, int64_t s_kv, int causal, int hq,
                       int hkv, int d, size_t room) {
-  const int cap = split_cap(s_q, hq, hkv);
-  if (cap <= 1 || s_q < 1) return {1, 0};
-  const int qrows = qrows_for(hq, hkv);
-  const int nqb = (int)((s_q + qrows - 1) / qrows);
-  const int heads = (int)(grid_size(s_q, hq, hkv) / nqb);
-  std::vector<int> nt(nqb);
-  int max_nt = 0;
-  for (int b = 0; b < nqb; ++b) {
-    const int64_t last = std::min<int64_t>((int64_t)(b + 1) * qrows, s_q) - 1;
-    const int64_t hi = causal ? std::min(q_off + last - k_off, s_kv - 1) : s_kv - 1;
-    nt[b] = hi >= 0 ? (int)(hi / BN + 1) : 0;
-    max_nt = std::max(max_nt, nt[b]);
-  }
-  // one tile of one workgroup is 8 * 32 rows * 64 keys * 4d FLOP; at about
-  // 4.3 TFLOP/s per compute unit and 5 TB/s that is worth d * 76 KB of traffic
-  const double bytes_per_tile = 76.0e3 * d;
-  double base = 0, best_cost = 0;
-  SplitPlan best{1, 0};
-  for (int z = 1; z <= cap; ++z) {
-    const int c = (max_nt + z - 1) / z;
-    if (z > 1 && (c < kMinSplitTiles || split_bytes(z, s_q, hq, d) > room)) break;
-    std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
-    for (int i = 0; i < kCUs; ++i) cu.push(0.0);
-    double makespan = 0, items = 0;
-    for (int y = 0; y < heads; ++y)
-      for (int b = nqb - 1; b >= 0; --b)
-        for (int k = 0; k < z; ++k) {
-          const int len = z > 1 ? std::min(nt[b] - k * c, c) : nt[b];
-          if (len <= 0) continue;
-          const double f = cu.top() + len + 0.5;  // 0.5: prologue and epilogue
-          cu.pop();
-          cu.push(f);
-          makespan = std::max(makespan, f);
-          items += 1;
-        }
-    double cost = makespan;
-    if (z > 1)  // partial O written and read back, final O written, launch
-      cost += 2.0 + (items * qrows * hg_for(hq / hkv) * d * 8.0 + (double)s_q * hq * d * 2) /
-                        bytes_per_tile;
-    if (z == 1) {
-      base = best_cost = cost;
-    } else if (cost < 0.85 * base && cost < best_cost) {
-      best_cost = cost;
-      best = {z, c};
-    }
-  }
-  return best;
+  int cap = split_cap(s_q, hq, hkv);
+  while (cap > 1 && split_bytes(cap, s_q, hq, d) > room) --cap;
+  SplitProblem sp{};
+  sp.s_q = s_q;
+  sp.q_off = q_off;
+  sp.k_off = k_off;
+  sp.s_kv = s_kv;
+  sp.causal = causal;
+  sp.qrows = qrows_for(hq, hkv);
+  sp.heads = (int)(grid_size(s_q, hq, hkv) / ((s_q + sp.qrows - 1) / sp.qrows));
+  sp.key_tile = BN;
+  sp.slots = kCUs;
+  sp.cap = cap;
+  sp.min_tiles = kMinSplitTiles;
+  // each (block, split) partial O is written and read back; the final O written
+  sp.item_bytes = (double)sp.qrows * hg_for(hq / hkv) * d * 8;
+  sp.fixed_bytes = (double)s_q * hq * d * 2;
+  sp.tile_bytes = 76.0e3 * d;
+  return plan_key_splits(sp);
 }
 
 template <int D, int HG>

@@ -145,11 +145,16 @@ int bwd_checked(const void* q, const void* k, const void* v, const void* o, cons
   const size_t qb = (size_t)s_q * hq * d * es, kb = (size_t)s_k * hkv * d * es;
   const size_t gqb = (size_t)s_q * hq * d * gs, gkb = (size_t)s_k * hkv * d * gs;
   const size_t lb = (size_t)s_q * hq * sizeof(float);
-  const size_t need = usp_attn_bwd_interval_workspace_bytes(s_q, s_k, hq, hkv, d, dtype);
+  // bf16: room beyond the required part (as much as the workspace query
+  // returns) lets a short call split dQ's keys
+  const size_t need = dtype == USP_BF16
+                          ? usp::attn_bwd_bf16_min_workspace(s_q, s_k, hq, hkv, d)
+                          : usp_attn_bwd_interval_workspace_bytes(s_q, s_k, hq, hkv, d, dtype);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return USP_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return USP_ERR_INVALID;
+  const size_t used = dtype == USP_BF16 ? workspace_bytes : need;
   const Span ins[] = {{q, qb}, {k, kb}, {v, kb}, {o, qb}, {lse, lb}, {dout, qb}};
-  const Span outs[] = {{dq, gqb}, {dk, gkb}, {dv, gkb}, {workspace, need}};
+  const Span outs[] = {{dq, gqb}, {dk, gkb}, {dv, gkb}, {workspace, need > 0 ? used : 0}};
   for (const Span& a : outs)
     for (const Span& b : ins)
       if (overlap(a, b)) return USP_ERR_INVALID;
@@ -159,7 +164,7 @@ int bwd_checked(const void* q, const void* k, const void* v, const void* o, cons
   usp::AttnArgs a = interval_args(s_q, q_off, s_k, k_off, s_k_valid, cu, n_docs, hq, hkv, d,
                                   scale, causal, stream);
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.workspace = workspace;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
   a.out_f32 = grad_dtype == USP_FP32;
   a.accumulate = accumulate;
   return dtype == USP_BF16 ? usp::attn_bwd_bf16(a) : usp::attn_bwd_f32(a);
@@ -281,6 +286,19 @@ int usp_attn_fwd_num_splits(int64_t s_q, int64_t q_off, int64_t s_k, int64_t k_o
                                   causal, nullptr);
   a.workspace_bytes = workspace_bytes;
   return usp::attn_fwd_bf16_splits(a);
+}
+
+int usp_attn_bwd_num_splits(int64_t s_q, int64_t q_off, int64_t s_k, int64_t k_off,
+                            int64_t s_k_valid, int hq, int hkv, int d, int causal, int dtype,
+                            size_t workspace_bytes) {
+  const int rc = check_interval(s_q, q_off, s_k, k_off, s_k_valid, nullptr, 0, hq, hkv, d, 1.0f,
+                                causal, dtype);
+  if (rc != USP_OK) return rc;
+  if (dtype != USP_BF16) return 1;
+  usp::AttnArgs a = interval_args(s_q, q_off, s_k, k_off, s_k_valid, nullptr, 0, hq, hkv, d, 1.0f,
+                                  causal, nullptr);
+  a.workspace_bytes = workspace_bytes;
+  return usp::attn_bwd_bf16_dq_splits(a);
 }
 
 int usp_attn_bwd_interval(const void* q, const void* k, const void* v, const void* o,

@@ -106,9 +106,31 @@ inline MaskGeom mask_geom(const AttnArgs& a) {
 int kmajor_launch(const void* src, void* dst, int64_t s_pad, int heads, int d, int64_t s_t,
                   hipStream_t stream, const char* trace_name);
 
+// Key splits of a query-stationary kernel (splits.hip): query blocks of qrows
+// rows over keys in tiles of key_tile, heads workgroups per block, slots
+// workgroups resident at once; at most cap splits of at least min_tiles tiles.
+// The combining kernel moves item_bytes per (block, split) it reads and
+// fixed_bytes once; tile_bytes is that traffic's worth in one tile-time of one
+// workgroup.
+struct SplitProblem {
+  int64_t s_q, q_off, k_off, s_kv;
+  int causal;
+  int qrows, heads, key_tile;
+  int slots, cap, min_tiles;
+  double item_bytes, fixed_bytes, tile_bytes;
+};
+struct SplitPlan {
+  int n_split, split_tiles;  // splits (1: none) and tiles per split
+};
+SplitPlan plan_key_splits(const SplitProblem& p);
+
 size_t attn_fwd_bf16_workspace(int64_t s_k, int hq, int hkv, int d);
 size_t attn_fwd_bf16_min_workspace(int64_t s_k, int hkv, int d);  // the V copy alone
 size_t attn_bwd_bf16_workspace(int64_t s_q, int64_t s_k, int hq, int hkv, int d);
+// the part without room for dQ key splits
+size_t attn_bwd_bf16_min_workspace(int64_t s_q, int64_t s_k, int hq, int hkv, int d);
+// Key splits the bf16 dQ kernel runs for these arguments (1: a single pass).
+int attn_bwd_bf16_dq_splits(const AttnArgs& a);
 int attn_fwd_bf16(const AttnArgs& a);
 // Key splits the bf16 forward runs for these arguments (1: a single pass).
 int attn_fwd_bf16_splits(const AttnArgs& a);
