@@ -213,6 +213,17 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
   const int wr_lo = key_rows(pr.m, min(wj0, s_k - 1)).lo;
   const int wr_hi = key_rows(pr.m, min(wj0 + 31, s_k - 1)).hi - 1;
 
+  const int tstart = (rstart / BQ) * BQ;
+  // this chunk's row tiles [clo, chi] (tile = BQ rows), chunks counted down
+  // from the last tile; with one chunk, every tile of [rstart, rend]
+  const int tlast = (s_q - 1) / BQ;
+  const int clo = max(tstart / BQ, tlast - (cch + 1) * pr.cht + 1);
+  const int chi = min(rend / BQ, tlast - cch * pr.cht);
+  const int ntr = (j0 < s_kv && rend >= rstart && chi >= clo) ? chi - clo + 1 : 0;
+  const int nt = ntr * g;
+  // a chunk with no rows writes no partial (the reduction skips it)
+  if (pr.part != nullptr && ntr == 0) return;
+
   // stationary fragment (B operand, lane = key): K for role 0, V for role 1
   bf16x8 sreg[KK];
   {
@@ -233,15 +244,6 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
   f32x16 acc[DB];  // dV^T (role 0) or dK^T (role 1): rows = d, cols = keys
 #pragma unroll
   for (int b = 0; b < DB; ++b) acc[b] = f32x16{};
-
-  const int tstart = (rstart / BQ) * BQ;
-  // this chunk's row tiles [clo, chi] (tile = BQ rows), chunks counted down
-  // from the last tile; with one chunk, every tile of [rstart, rend]
-  const int tlast = (s_q - 1) / BQ;
-  const int clo = max(tstart / BQ, tlast - (cch + 1) * pr.cht + 1);
-  const int chi = min(rend / BQ, tlast - cch * pr.cht);
-  const int ntr = (j0 < s_kv && rend >= rstart && chi >= clo) ? chi - clo + 1 : 0;
-  const int nt = ntr * g;
 
   // Tile order: query tiles from the END of the sequence downwards, the heads
   // of the group innermost. Every resident workgroup then reads the same
@@ -479,18 +481,34 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
 }
 
 // dV and dK from the row chunks' partial sums, added in chunk order (the
-// result does not depend on scheduling). One thread per 4 values; n4 values
-// of 4 per tensor.
+// result does not depend on scheduling). Only the chunks holding rows of the
+// key's block wrote a partial; which ones is found from the mask geometry
+// with the dK/dV kernel's own arithmetic (keys_per_block keys per block,
+// tiles of bq rows, cht tiles per chunk counted down from the last tile). One
+// thread per 4 values; n4 values of 4 per tensor, key4 of them per key.
 __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restrict__ part,
                                                           void* dv, void* dk, int64_t n4,
-                                                          int n_ch, int f32, int accum) {
+                                                          int n_ch, int f32, int accum,
+                                                          MaskGeom m, int keys_per_block, int bq,
+                                                          int cht, int key4) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= 2 * n4) return;
   const int t = i >= n4 ? 1 : 0;  // 0: dV, 1: dK
   const int64_t e = i - t * n4;
+  const int key = (int)(e / key4);
+  const int j0 = key / keys_per_block * keys_per_block;
+  const int j1 = min(j0 + keys_per_block, m.s_k);
+  const RowSpan rfirst = key_rows(m, j0), rlast = key_rows(m, j1 - 1);
+  const int rstart = max(rfirst.lo, 0), rend = rlast.hi - 1;
+  const int tfirst = rstart / bq, tlast = (m.s_q - 1) / bq;
+  const bool rows = j0 < m.s_kv && rend >= rstart;
   const f32x4* src = reinterpret_cast<const f32x4*>(part) + (int64_t)t * n_ch * n4 + e;
-  f32x4 acc = src[0];
-  for (int c = 1; c < n_ch; ++c) acc += src[(int64_t)c * n4];
+  f32x4 acc = {};
+  for (int c = 0; c < n_ch; ++c) {
+    const int clo = max(tfirst, tlast - (c + 1) * cht + 1);
+    const int chi = min(rend / bq, tlast - c * cht);
+    if (rows && chi >= clo) acc += src[(int64_t)c * n4];
+  }
   void* out = t ? dk : dv;
   if (f32) {
     f32x4* o = reinterpret_cast<f32x4*>(out) + e;
@@ -876,7 +894,8 @@ int bwd_launch(const BwdParams& p, const AttnArgs& a, float* dd, float* lse2, fl
       TraceScope ts("attn_bwd_dkdv_reduce", a.stream);
       hipLaunchKernelGGL(dkdv_reduce_kernel, dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256), 0,
                          a.stream, static_cast<const float*>(part), a.dv, a.dk, n4, pk.n_ch,
-                         a.out_f32, a.accumulate);
+                         a.out_f32, a.accumulate, pk.m, keys, kDkdvRows, pk.cht,
+                         (int)(a.hkv * D / 4));
       if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
     }
   }
