@@ -230,12 +230,12 @@ def test_merge_argument_errors(L):
 
 def dkdv_chunks(s_q, s_k, hkv):
     """Row chunks per key block of the bf16 dK/dV kernel: 1 when the 128-key
-    blocks give at least 512 workgroups, else enough for about 1024 (block,
+    blocks give at least 512 workgroups, else enough for about 2048 (block,
     chunk) items, at most 16 and at most the number of 64-row tiles."""
     items = -(-s_k // 128) * hkv
     if items >= 512:
         return 1
-    return max(1, min(-(-1024 // items), -(-s_q // 64), 16))
+    return max(1, min(-(-2048 // items), -(-s_q // 64), 16))
 
 
 def dq_split_cap(s_q, hq, hkv):
@@ -264,7 +264,7 @@ def test_workspace_sizes(L):
         # D and LSE * log2(e) per (head, row), fp32
         assert 2 * 4 * s * 4 <= b - part < 2 * 4 * (s + 128) * 4 + 512
     assert dkdv_chunks(120000, 120000, 1) == 1 and dkdv_chunks(8192, 8192, 1) == 16
-    assert dkdv_chunks(32768, 32768, 1) == 4 and dkdv_chunks(100, 100, 1) == 2
+    assert dkdv_chunks(32768, 32768, 1) == 8 and dkdv_chunks(100, 100, 1) == 2
     assert L.usp_attn_fwd_workspace_bytes(512, 4, 2, 64, FP32) == 0
     assert L.usp_attn_bwd_workspace_bytes(512, 4, 2, 64, FP32) == 512 * 4 * 4
     assert L.usp_attn_fwd_workspace_bytes(0, 4, 1, 128, BF16) == 0
