@@ -553,9 +553,11 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
   const int chunks = g / HG;
   const int kvh = blockIdx.y / chunks, hc = blockIdx.y % chunks;
   const int head = kvh * g + hc * HG + (w % HG);
-  // heaviest query block first; its key splits follow one another
+  // heaviest query block first; its key splits follow one another, the
+  // order rotated by the block when their count is even (see the forward)
   const int qb = pr.n_blocks - 1 - (int)blockIdx.x / pr.dq_split;
-  const int zs = (int)blockIdx.x % pr.dq_split;
+  const int zk = (int)blockIdx.x % pr.dq_split;
+  const int zs = (pr.dq_split & 1) ? zk : (zk + qb) % pr.dq_split;
   const int q0 = qb * QROWS;
   const int q1 = min(q0 + QROWS, s_q);
   const int wq0 = q0 + (w / HG) * 32;

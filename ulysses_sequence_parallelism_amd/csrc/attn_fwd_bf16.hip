@@ -109,9 +109,13 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
   const int chunks = g / HG;
   const int kvh = blockIdx.y / chunks, hc = blockIdx.y % chunks;
   const int head = kvh * g + hc * HG + (w % HG);
-  // heaviest query block first; its key splits follow one another
+  // heaviest query block first; its key splits follow one another. With an
+  // even count the order is rotated by the block, so that the round-robin
+  // over the 8 dies does not send every block's first piece to the same dies
+  // (an odd count is coprime with 8 and keeps the full pieces first).
   const int qb = pr.n_qblocks - 1 - (int)blockIdx.x / pr.n_split;
-  const int zs = (int)blockIdx.x % pr.n_split;
+  const int zk = (int)blockIdx.x % pr.n_split;
+  const int zs = (pr.n_split & 1) ? zk : (zk + qb) % pr.n_split;
   const int q0 = qb * QROWS;
   const int s_q = pr.m.s_q, s_k = pr.m.s_k;
   const int q1 = min(q0 + QROWS, s_q);

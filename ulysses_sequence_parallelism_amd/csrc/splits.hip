@@ -30,26 +30,36 @@ SplitPlan plan_key_splits(const SplitProblem& p) {
     nt[b] = hi >= 0 ? (int)(hi / p.key_tile + 1) : 0;
     max_nt = std::max(max_nt, nt[b]);
   }
-  // Each candidate is scored by simulating the hardware's in-order dispatch
-  // of the grid (query blocks heaviest first, a block's splits consecutive)
-  // onto p.slots resident workgroups, in tile-times of one workgroup, plus
-  // the combining kernel's traffic in the same unit. Splitting must save 15%.
+  // Each candidate is scored by simulating the hardware's dispatch of the
+  // grid, in tile-times of one workgroup: workgroups go round-robin to the
+  // kXcds dies by linear index, and each die hands its next workgroup to the
+  // first of its slots that frees. The grid runs query blocks heaviest first,
+  // a block's splits adjacent in the order the kernels use: k for an odd Z,
+  // (k + block) mod Z for an even one, so that no die receives only the
+  // first (full) piece of every block. The combining kernel's traffic is
+  // added in the same unit. Splitting must save 15%.
+  constexpr int kXcds = 8;
   double base = 0, best_cost = 0;
   SplitPlan best{1, 0};
   for (int z = 1; z <= p.cap; ++z) {
     const int c = (max_nt + z - 1) / z;
     if (z > 1 && c < p.min_tiles) break;
-    std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
-    for (int i = 0; i < p.slots; ++i) free_at.push(0.0);
+    std::vector<std::priority_queue<double, std::vector<double>, std::greater<double>>> free_at(
+        kXcds);
+    for (int x = 0; x < kXcds; ++x)
+      for (int i = 0; i < p.slots / kXcds; ++i) free_at[x].push(0.0);
     double makespan = 0, items = 0;
+    int64_t idx = 0;
     for (int y = 0; y < p.heads; ++y)
       for (int b = nqb - 1; b >= 0; --b)
-        for (int k = 0; k < z; ++k) {
-          const int len = z > 1 ? std::min(nt[b] - k * c, c) : nt[b];
+        for (int k = 0; k < z; ++k, ++idx) {
+          const int piece = (z & 1) ? k : (k + b) % z;
+          const int len = z > 1 ? std::min(nt[b] - piece * c, c) : nt[b];
           if (len <= 0) continue;
-          const double f = free_at.top() + len + 0.5;  // 0.5: prologue and epilogue
-          free_at.pop();
-          free_at.push(f);
+          auto& q = free_at[idx % kXcds];
+          const double f = q.top() + len + 0.5;  // 0.5: prologue and epilogue
+          q.pop();
+          q.push(f);
           makespan = std::max(makespan, f);
           items += 1;
         }
