@@ -33,6 +33,14 @@
 //   * Tiles go straight from global memory into double-buffered, swizzled LDS
 //     slots; masks are applied only on boundary tiles, and the causal
 //     triangle is launched heaviest-first.
+//   * Short sequences, where either grid would leave compute units idle and
+//     the causal triangle's longest blocks would set the time: the dK/dV
+//     kernel splits each key block's rows into chunks, and the dQ kernel
+//     splits each query block's keys (planned in splits.hip). Each piece
+//     writes an fp32 partial sum into the workspace, and a reduction adds
+//     them in a fixed order, so the result still does not depend on
+//     scheduling. Pieces with nothing to do write nothing; the reductions
+//     find the others from the mask geometry.
 #include <algorithm>
 #include <type_traits>
 

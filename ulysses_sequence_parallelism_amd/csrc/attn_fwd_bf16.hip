@@ -53,6 +53,10 @@
 //     a boundary; tiles entirely outside every row's range are never visited.
 //   * Workgroups are launched heaviest-first (last query block first) so the
 //     causal triangle's long rows start early and the tail is short.
+//   * Short sequences (a grid of a few hundred workgroups) split each query
+//     block's key tiles into consecutive pieces run by separate workgroups
+//     (planned in splits.hip); each writes an fp32 partial O and its LSE, and
+//     a merge kernel combines them exactly, as the merge of ring steps does.
 #include <algorithm>
 #include <type_traits>
 
