@@ -341,6 +341,36 @@ def test_fwd_workspace_and_key_splits(L):
     assert L.usp_attn_fwd_num_splits(8, 0, 8, 0, 9, 4, 1, 128, 1, BF16, 1 << 30) == -1
 
 
+def test_key_split_plans_fit_the_workspace(L):
+    """Whatever workspace a caller passes (at least the required part), the
+    planned splits' partials fit inside it: forward O + LSE per split after
+    the V copy, dQ per split after the backward's required part. Swept over
+    interval shapes (more rows than keys, offsets), masks, head layouts and
+    workspace sizes from the minimum to the query's size and beyond."""
+    import itertools
+    vcopy = lambda s_k, hkv, d: hkv * d * ((s_k + 127) // 128 * 128) * 2
+    shapes = [(8192, 0, 8192, 0), (3000, 0, 1000, 500), (1500, 2000, 3500, 0), (700, 0, 5000, 0),
+              (16384, 0, 16384, 0), (4096, 4096, 4096, 0), (100, 0, 100, 0)]
+    for (s_q, q_off, s_k, k_off), (hq, hkv, d), causal in itertools.product(
+            shapes, ((4, 1, 128), (16, 4, 64), (8, 1, 128), (2, 2, 64)), (0, 1)):
+        fq = L.usp_attn_fwd_workspace_bytes(s_k, hq, hkv, d, BF16)
+        bq = L.usp_attn_bwd_interval_workspace_bytes(s_q, s_k, hq, hkv, d, BF16)
+        f_min = vcopy(s_k, hkv, d)
+        b_min = bq - dq_room(s_q, hq, hkv, d)
+        for frac in (0.0, 0.3, 0.7, 1.0, 2.0):
+            fw = int(f_min + frac * max(fq - f_min, s_q * hq * d * 8))
+            z = L.usp_attn_fwd_num_splits(s_q, q_off, s_k, k_off, s_k, hq, hkv, d, causal, BF16, fw)
+            assert z >= 1
+            if z > 1:
+                need = -(-z * s_q * hq * d * 4 // 256) * 256 + z * hq * s_q * 4
+                assert f_min + need <= fw, (s_q, s_k, hq, hkv, d, causal, fw, z)
+            bw = int(b_min + frac * max(bq - b_min, s_q * hq * d * 8))
+            z = L.usp_attn_bwd_num_splits(s_q, q_off, s_k, k_off, s_k, hq, hkv, d, causal, BF16, bw)
+            assert z >= 1
+            if z > 1:
+                assert b_min + z * s_q * hq * d * 4 <= bw, (s_q, s_k, hq, hkv, d, causal, bw, z)
+
+
 def test_fast_division_host_side(tmp_path):
     """The pack/unpack kernels divide by run and row lengths with a
     multiply-high reciprocal; check it exhaustively on small values and on
