@@ -94,9 +94,10 @@ int usp_unpack_head2seq(const void* y, void* x, int64_t s_real, int p, int h, in
  * key-major copy of V there and, when s_pad rows make a grid of fewer than 512
  * workgroups (short sequences), room for up to 8 key splits: fp32 partial O
  * and LSE of every query row, combined exactly by a merge kernel (see
- * usp_attn_fwd_num_splits). About 135 MB at s_pad = 8192 with 4 query heads and
- * d = 128; nothing beyond the V copy from 16,384 query rows per KV head at 4:1
- * GQA upwards.
+ * usp_attn_fwd_num_splits). The room is for min(8, ceil(1024 / workgroups))
+ * splits: about 135 MB at s_pad = 8192 with 4 query heads, one KV head and
+ * d = 128 (8 splits) or at 16,384 (4 splits); none from 32,768 rows per KV
+ * head at 4:1 GQA upwards.
  */
 size_t usp_attn_fwd_workspace_bytes(int64_t s_pad, int hq, int hkv, int d, int dtype);
 
