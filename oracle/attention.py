@@ -177,47 +177,60 @@ def attn_bwd_rows(q, k, v, do, rows, scale, s_valid=None, cu_seqlens=None, causa
     return dq
 
 
-def attn_bwd_keys(q, k, v, do, keys, scale, s_valid=None, cu_seqlens=None, causal=True):
-    """dK and dV for the selected key rows only: ([len(keys), Hkv, d] x 2).
+def attn_bwd_keys(q, k, v, do, keys, scale, s_valid=None, cu_seqlens=None, causal=True,
+                  q_lo=0, q_hi=None):
+    """dK and dV for the selected key rows only: ([len(keys), Hkv, d] x 2),
+    from the query rows [q_lo, q_hi) (default: all rows; a smaller interval
+    gives that interval's contribution, e.g. one ring or context-parallel
+    rank's rows).
 
-    Every query row i whose allowed set M(i) contains one of the keys is
-    recomputed in full (LSE and D need the whole row), so this is cheap only
-    when few rows see those keys, e.g. keys near the end of a causal
-    sequence or of a document."""
+    Every query row of the interval whose allowed set M(i) contains one of
+    the keys needs LSE_i and D_i = dO_i . O_i over its WHOLE row, so those
+    rows are run through attn_fwd_rows first; the gradient terms are then
+    formed for the selected key columns only:
+        dK_j = scale sum_h sum_i P_ij (dP_ij - D_i) q_i,  dV_j = sum_h sum_i P_ij dO_i."""
     q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
     s, hq, hkv, d, g = _check(q, k, v)
     s_valid = s if s_valid is None else s_valid
+    q_hi = s if q_hi is None else q_hi
     doc = doc_of(s, cu_seqlens)
     keys = np.asarray(keys, dtype=np.int64)
-    # rows that see at least one selected key
-    cand = np.arange(int(keys.min()) if causal else 0, s)
-    seen = np.zeros(len(cand), dtype=bool)
-    for j0 in range(0, len(keys), 64):
-        kj = keys[j0:j0 + 64]
-        m = np.ones((len(cand), len(kj)), dtype=bool)
-        m &= (kj < s_valid)[None, :]
-        if causal:
-            m &= kj[None, :] <= cand[:, None]
-        if doc is not None:
-            m &= doc[kj][None, :] == doc[cand][:, None]
-        seen |= m.any(axis=1)
-    rows = cand[seen]
     dk = np.zeros((len(keys), hkv, d))
     dv = np.zeros((len(keys), hkv, d))
+    # rows of the interval that see at least one selected key
+    cand = np.arange(max(q_lo, int(keys.min()) if causal else q_lo), q_hi)
+    if len(cand) == 0:
+        return dk, dv
+    seen = np.zeros(len(cand), dtype=bool)
+    for r0 in range(0, len(cand), 4096):
+        seen[r0:r0 + 4096] = _sees(cand[r0:r0 + 4096], keys, s_valid, doc, causal).any(axis=1)
+    rows = cand[seen]
     if len(rows) == 0:
         return dk, dv
-    _, lse = attn_fwd_rows(q, k, v, rows, scale, s_valid, cu_seqlens, causal)
+    o, lse = attn_fwd_rows(q, k, v, rows, scale, s_valid, cu_seqlens, causal)
+    dd = np.einsum("rhd,rhd->hr", do[rows], o)          # D_i = dO_i . O_i, [Hq, rows]
     for b0 in range(0, len(rows), ROW_BLOCK):
         rb = rows[b0:b0 + ROW_BLOCK]
+        m = _sees(rb, keys, s_valid, doc, causal)          # [rows, keys]
         for h in range(hq):
             kvh = h // g
-            nc, p, ds = _bwd_block(q, k, v, do, h, kvh, rb, lse[h, b0:b0 + len(rb)],
-                                   scale, s_valid, doc, causal, s)
-            sel = keys < nc
-            ks = keys[sel]
-            dk[sel, kvh, :] += scale * (ds[:, ks].T @ q[rb, h, :])
-            dv[sel, kvh, :] += p[:, ks].T @ do[rb, h, :]
+            z = scale * (q[rb, h, :] @ k[keys, kvh, :].T)
+            p = np.where(m, np.exp(np.where(m, z, 0.0) - lse[h, b0:b0 + len(rb)][:, None]), 0.0)
+            dp = do[rb, h, :] @ v[keys, kvh, :].T
+            ds = p * (dp - dd[h, b0:b0 + len(rb)][:, None])
+            dk[:, kvh, :] += scale * (ds.T @ q[rb, h, :])
+            dv[:, kvh, :] += p.T @ do[rb, h, :]
     return dk, dv
+
+
+def _sees(rows, keys, s_valid, doc, causal):
+    """Boolean [len(rows), len(keys)]: key keys[b] is in M(rows[a])."""
+    m = np.broadcast_to((keys < s_valid)[None, :], (len(rows), len(keys))).copy()
+    if causal:
+        m &= keys[None, :] <= rows[:, None]
+    if doc is not None:
+        m &= doc[keys][None, :] == doc[rows][:, None]
+    return m
 
 
 # ---------------------------------------------------------------------------

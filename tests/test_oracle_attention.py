@@ -260,3 +260,22 @@ def test_planted_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(A, "_scores", wrong_group)
     o, lse = oracle.attn_fwd(q, k, v, scale, s_valid, cu, causal)
     assert not np.allclose(o, ref[0], atol=1e-6)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_sampled_keys_of_a_query_interval_match_torch(case):
+    """attn_bwd_keys over a query interval [q_lo, q_hi) is that interval's
+    contribution to dK / dV: the gradient of sum over the interval's rows of
+    O * dO, i.e. torch autograd with dO set to zero outside the interval."""
+    name, s, s_valid, hq, hkv, d, cu, causal = case
+    q, k, v, do = (rand((s, h, d), 90 + seed) for seed, h in zip(range(4), (hq, hkv, hkv, hq)))
+    scale = 1.0 / np.sqrt(d)
+    keys = np.array(sorted({0, 1, 2, s // 3, s // 2, s - 5, s - 2, s - 1}))
+    for q_lo, q_hi in ((0, s), (s // 4, s), (s // 3, 2 * s // 3), (s - 1, s)):
+        do_i = np.zeros_like(do)
+        do_i[q_lo:q_hi] = do[q_lo:q_hi]
+        _, _, _, rdk, rdv = torch_reference(q, k, v, do_i, scale, s_valid, cu, causal)
+        dk, dv = oracle.attn_bwd_keys(q, k, v, do, keys, scale, s_valid, cu, causal,
+                                      q_lo=q_lo, q_hi=q_hi)
+        np.testing.assert_allclose(dk, rdk[keys], atol=RTOL_LIB)
+        np.testing.assert_allclose(dv, rdv[keys], atol=RTOL_LIB)

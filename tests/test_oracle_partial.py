@@ -13,7 +13,7 @@ def rand(shape, seed):
     return np.random.default_rng(seed).standard_normal(shape)
 
 
-def torch_full(q, k, v, do, scale, cu, causal):
+def torch_full(q, k, v, do, scale, cu, causal, s_valid=None):
     s, hq, d = q.shape
     g = hq // k.shape[1]
     doc = np.zeros(s, dtype=np.int64)
@@ -24,6 +24,8 @@ def torch_full(q, k, v, do, scale, cu, causal):
     mask = doc[:, None] == doc[None, :]
     if causal:
         mask &= idx[None, :] <= idx[:, None]
+    if s_valid is not None:
+        mask &= idx[None, :] < s_valid
     tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
     o = torch.nn.functional.scaled_dot_product_attention(
         tq.transpose(0, 1), tk.repeat_interleave(g, 1).transpose(0, 1),
@@ -113,3 +115,57 @@ def test_contiguous_query_interval_equals_rows_of_full_attention():
         o, lse = oracle.attn_fwd_partial(q[qa:qb], k, v, 0.3, q_off=qa, k_off=0)
         np.testing.assert_allclose(o, o_ref[qa:qb], atol=1e-13)
         np.testing.assert_allclose(lse, lse_ref[:, qa:qb], atol=1e-13)
+
+
+# Padded keys inside the intervals: with S_valid < S the last key block (or
+# more) holds keys past the real sequence, which must be masked; the interval
+# functions take that as sk_valid = the valid keys of the block. Padded query
+# rows are computed like any other row.
+PAD_CASES = [
+    # S, S_valid, hq, hkv, key chunk edges, query chunk edges, causal
+    (96, 90, 4, 2, [0, 40, 64, 96], [0, 33, 96], True),           # last block 26 of 32 valid
+    (80, 70, 4, 1, [0, 16, 32, 48, 64, 80], [0, 40, 80], True),   # ring of 5, last block 6 of 16
+    (50, 40, 2, 2, [0, 40, 50], [0, 25, 50], True),               # last block entirely padding
+    (64, 60, 4, 2, [0, 20, 64], [0, 10, 64], False),
+    (72, 65, 2, 1, [0, 64, 72], [0, 72], False),                  # last block with one valid key
+]
+
+
+@pytest.mark.parametrize("case", PAD_CASES)
+def test_interval_split_with_padded_keys_recombines_to_full_attention(case):
+    s, s_valid, hq, hkv, kedges, qedges, causal = case
+    d, scale = 16, 0.3
+    q, k, v, do = (rand((s, h, d), 600 + i) for i, h in enumerate((hq, hkv, hkv, hq)))
+    ro, rdq, rdk, rdv = torch_full(q, k, v, do, scale, None, causal, s_valid=s_valid)
+    o_full = np.zeros_like(q)
+    lse_full = np.zeros((hq, s))
+    for qa, qb in zip(qedges[:-1], qedges[1:]):
+        parts = []
+        for ka, kb in zip(kedges[:-1], kedges[1:]):
+            skv = min(max(s_valid - ka, 0), kb - ka)
+            o_p, lse_p = oracle.attn_fwd_partial(q[qa:qb], k[ka:kb], v[ka:kb], scale, q_off=qa,
+                                                 k_off=ka, sk_valid=skv, causal=causal)
+            if skv == 0:
+                assert np.isneginf(lse_p).all() and (o_p == 0).all()
+            parts.append((o_p, lse_p))
+        o_full[qa:qb], lse_full[:, qa:qb] = oracle.lse_merge(parts)
+    np.testing.assert_allclose(o_full, ro, atol=1e-12)
+    _, lse_ref = oracle.attn_fwd(q, k, v, scale, s_valid, None, causal)
+    np.testing.assert_allclose(lse_full, lse_ref, atol=1e-12)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for qa, qb in zip(qedges[:-1], qedges[1:]):
+        for ka, kb in zip(kedges[:-1], kedges[1:]):
+            skv = min(max(s_valid - ka, 0), kb - ka)
+            a, b, c = oracle.attn_bwd_partial(q[qa:qb], k[ka:kb], v[ka:kb], o_full[qa:qb],
+                                              lse_full[:, qa:qb], do[qa:qb], scale, q_off=qa,
+                                              k_off=ka, sk_valid=skv, causal=causal)
+            dq[qa:qb] += a
+            dk[ka:kb] += b
+            dv[ka:kb] += c
+    np.testing.assert_allclose(dq, rdq, atol=1e-10)
+    np.testing.assert_allclose(dk, rdk, atol=1e-10)
+    np.testing.assert_allclose(dv, rdv, atol=1e-10)
+    # padded keys get no gradient at all
+    assert (dk[s_valid:] == 0).all() and (dv[s_valid:] == 0).all()

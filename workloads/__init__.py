@@ -129,15 +129,34 @@ def cu_seqlens(lengths) -> np.ndarray:
     return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
 
 
-def row_sample(w: Workload, n_uniform: int = 256, edge: int = 32,
-               boundaries=()) -> np.ndarray:
-    """Query rows checked at full size: both ends, both sides of every
-    boundary (slice or document), and seeded uniform rows."""
-    s = w.s_pad
-    rows = set(range(min(edge, s)))
-    rows.update(range(max(0, s - edge), s))
+def index_sample(n: int, seed, n_uniform: int = 1024, edge: int = 64, boundaries=(),
+                 lo: int = 0) -> np.ndarray:
+    """Sorted distinct indexes in [lo, n): the first and last ``edge``, +-2
+    around every boundary inside the range, and ``n_uniform`` seeded uniform
+    draws from ``np.random.default_rng(seed)``."""
+    idx = set(range(lo, min(lo + edge, n)))
+    idx.update(range(max(lo, n - edge), n))
     for b in boundaries:
-        rows.update(i for i in range(b - 2, b + 3) if 0 <= i < s)
-    g = rng(w.cfg, w.variant, ROWS)
-    rows.update(int(i) for i in g.integers(0, s, size=n_uniform))
-    return np.array(sorted(rows), dtype=np.int64)
+        idx.update(i for i in range(b - 2, b + 3) if lo <= i < n)
+    g = np.random.default_rng(seed)
+    idx.update(int(i) for i in g.integers(lo, n, size=n_uniform))
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+def sample_boundaries(w: Workload) -> list[int]:
+    """Slice boundaries of the rank's share and, for packed documents, the
+    document boundaries: the positions the full-size samples straddle."""
+    b = [r * (w.s_pad // w.p) for r in range(1, w.p)]
+    if w.thd:
+        b += [int(c) for c in cu_seqlens(doc_lengths(w.s))[1:-1]]
+    return sorted(set(b))
+
+
+def row_sample(w: Workload, n_uniform: int = 1024, edge: int = 64,
+               boundaries=None) -> np.ndarray:
+    """Rows (and the same set as keys) checked at full size: both ends, both
+    sides of every slice or document boundary, and seeded uniform rows
+    (seed [cfg, variant, 9])."""
+    if boundaries is None:
+        boundaries = sample_boundaries(w)
+    return index_sample(w.s_pad, [w.cfg, w.variant, ROWS], n_uniform, edge, boundaries)
