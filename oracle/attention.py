@@ -81,11 +81,11 @@ def _check(q, k, v):
     return s, hq, hkv, d, hq // hkv
 
 
-def _scores(q, k, h, kvh, rows, ncols, scale, s_valid, doc, causal):
-    """z for the given rows of head h against keys [0, ncols), with -inf off
-    M(i)."""
-    z = scale * (q[rows, h, :] @ k[:ncols, kvh, :].T)
-    z[~allowed_keys(rows, ncols, s_valid, doc, causal)] = -np.inf
+def _scores(q, k, h, kvh, rows, ncols, scale, s_valid, doc, causal, c0=0):
+    """z for the given rows of head h against keys [c0, ncols), with -inf off
+    M(i) (keys before c0 are outside every row's M(i))."""
+    z = scale * (q[rows, h, :] @ k[c0:ncols, kvh, :].T)
+    z[~allowed_keys(rows, ncols, s_valid, doc, causal)[:, c0:]] = -np.inf
     return z
 
 
@@ -93,9 +93,37 @@ def _ncols(rows, s, causal):
     return int(rows.max()) + 1 if causal else s
 
 
-def attn_fwd_rows(q, k, v, rows, scale, s_valid=None, cu_seqlens=None, causal=True):
+def _blocks(rows, doc):
+    """Index ranges [a, b) of consecutive entries of `rows`, at most ROW_BLOCK
+    long and, with documents, all in one document (so a block's keys start
+    at that document's start)."""
+    n = len(rows)
+    if doc is None:
+        return [(a, min(n, a + ROW_BLOCK)) for a in range(0, n, ROW_BLOCK)]
+    d = doc[rows]
+    cuts = [0] + [i for i in range(1, n) if d[i] != d[i - 1]] + [n]
+    out = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        out += [(x, min(b, x + ROW_BLOCK)) for x in range(a, b, ROW_BLOCK)]
+    return out
+
+
+def _col0(rows, doc):
+    """First key any of the rows may see: the start of the earliest row's
+    document (0 without documents)."""
+    if doc is None:
+        return 0
+    d0 = doc[int(rows.min())]
+    return int(np.searchsorted(doc, d0))
+
+
+def attn_fwd_rows(q, k, v, rows, scale, s_valid=None, cu_seqlens=None, causal=True,
+                  with_abs=False):
     """O and LSE for the selected query rows only: ([len(rows), Hq, d],
-    [Hq, len(rows)]). Each row costs O(S d)."""
+    [Hq, len(rows)]). Each row costs O(S d).
+
+    with_abs: also return sum_j P_ij |v_j| ([len(rows), Hq, d]), the sum of
+    the absolute terms of O (its size when every term had the same sign)."""
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     s, hq, hkv, d, g = _check(q, k, v)
     s_valid = s if s_valid is None else s_valid
@@ -103,18 +131,22 @@ def attn_fwd_rows(q, k, v, rows, scale, s_valid=None, cu_seqlens=None, causal=Tr
     rows = np.asarray(rows, dtype=np.int64)
     o = np.zeros((len(rows), hq, d))
     lse = np.zeros((hq, len(rows)))
-    for b0 in range(0, len(rows), ROW_BLOCK):
-        rb = rows[b0:b0 + ROW_BLOCK]
+    oabs = np.zeros((len(rows), hq, d)) if with_abs else None
+    for b0, b1 in _blocks(rows, doc):
+        rb = rows[b0:b1]
         nc = _ncols(rb, s, causal)
+        c0 = _col0(rb, doc)
         for h in range(hq):
-            z = _scores(q, k, h, h // g, rb, nc, scale, s_valid, doc, causal)
+            z = _scores(q, k, h, h // g, rb, nc, scale, s_valid, doc, causal, c0)
             m = z.max(axis=1)
             l = np.exp(z - m[:, None]).sum(axis=1)
             lse_b = m + np.log(l)
             p = np.exp(z - lse_b[:, None])
-            o[b0:b0 + len(rb), h, :] = p @ v[:nc, h // g, :]
+            o[b0:b0 + len(rb), h, :] = p @ v[c0:nc, h // g, :]
             lse[h, b0:b0 + len(rb)] = lse_b
-    return o, lse
+            if with_abs:
+                oabs[b0:b0 + len(rb), h, :] = p @ np.abs(v[c0:nc, h // g, :])
+    return (o, lse, oabs) if with_abs else (o, lse)
 
 
 def attn_fwd(q, k, v, scale, s_valid=None, cu_seqlens=None, causal=True):
@@ -124,13 +156,15 @@ def attn_fwd(q, k, v, scale, s_valid=None, cu_seqlens=None, causal=True):
 
 
 def _bwd_block(q, k, v, do, h, kvh, rb, lse_b, scale, s_valid, doc, causal, s):
+    """P and dS of the rows rb of head h over keys [c0, nc)."""
     nc = _ncols(rb, s, causal)
-    z = _scores(q, k, h, kvh, rb, nc, scale, s_valid, doc, causal)
+    c0 = _col0(rb, doc)
+    z = _scores(q, k, h, kvh, rb, nc, scale, s_valid, doc, causal, c0)
     p = np.exp(z - lse_b[:, None])
-    dp = do[rb, h, :] @ v[:nc, kvh, :].T
+    dp = do[rb, h, :] @ v[c0:nc, kvh, :].T
     dd = (p * dp).sum(axis=1)
     ds = p * (dp - dd[:, None])
-    return nc, p, ds
+    return c0, nc, p, ds
 
 
 def attn_bwd(q, k, v, o, lse, do, scale, s_valid=None, cu_seqlens=None, causal=True):
@@ -150,35 +184,38 @@ def attn_bwd(q, k, v, o, lse, do, scale, s_valid=None, cu_seqlens=None, causal=T
         rb = np.arange(b0, min(s, b0 + ROW_BLOCK))
         for h in range(hq):
             kvh = h // g
-            nc, p, ds = _bwd_block(q, k, v, do, h, kvh, rb, lse[h, rb], scale,
-                                   s_valid, doc, causal, s)
-            dq[rb, h, :] = scale * (ds @ k[:nc, kvh, :])
-            dk[:nc, kvh, :] += scale * (ds.T @ q[rb, h, :])
-            dv[:nc, kvh, :] += p.T @ do[rb, h, :]
+            c0, nc, p, ds = _bwd_block(q, k, v, do, h, kvh, rb, lse[h, rb], scale,
+                                       s_valid, doc, causal, s)
+            dq[rb, h, :] = scale * (ds @ k[c0:nc, kvh, :])
+            dk[c0:nc, kvh, :] += scale * (ds.T @ q[rb, h, :])
+            dv[c0:nc, kvh, :] += p.T @ do[rb, h, :]
     return dq, dk, dv
 
 
-def attn_bwd_rows(q, k, v, do, rows, scale, s_valid=None, cu_seqlens=None, causal=True):
-    """dQ for the selected query rows only: [len(rows), Hq, d]. LSE of those
-    rows is recomputed here, so no full forward is needed."""
+def attn_bwd_rows(q, k, v, do, rows, scale, s_valid=None, cu_seqlens=None, causal=True,
+                  lse=None):
+    """dQ for the selected query rows only: [len(rows), Hq, d]. The rows'
+    LSE [Hq, len(rows)] is the oracle's own (attn_fwd_rows of the same rows,
+    recomputed here when not given), so no full forward is needed."""
     q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
     s, hq, hkv, d, g = _check(q, k, v)
     s_valid = s if s_valid is None else s_valid
     doc = doc_of(s, cu_seqlens)
     rows = np.asarray(rows, dtype=np.int64)
-    _, lse = attn_fwd_rows(q, k, v, rows, scale, s_valid, cu_seqlens, causal)
+    if lse is None:
+        _, lse = attn_fwd_rows(q, k, v, rows, scale, s_valid, cu_seqlens, causal)
     dq = np.zeros((len(rows), hq, d))
-    for b0 in range(0, len(rows), ROW_BLOCK):
-        rb = rows[b0:b0 + ROW_BLOCK]
+    for b0, b1 in _blocks(rows, doc):
+        rb = rows[b0:b1]
         for h in range(hq):
-            nc, _, ds = _bwd_block(q, k, v, do, h, h // g, rb, lse[h, b0:b0 + len(rb)],
-                                   scale, s_valid, doc, causal, s)
-            dq[b0:b0 + len(rb), h, :] = scale * (ds @ k[:nc, h // g, :])
+            c0, nc, _, ds = _bwd_block(q, k, v, do, h, h // g, rb, lse[h, b0:b0 + len(rb)],
+                                       scale, s_valid, doc, causal, s)
+            dq[b0:b0 + len(rb), h, :] = scale * (ds @ k[c0:nc, h // g, :])
     return dq
 
 
 def attn_bwd_keys(q, k, v, do, keys, scale, s_valid=None, cu_seqlens=None, causal=True,
-                  q_lo=0, q_hi=None):
+                  q_lo=0, q_hi=None, with_abs=False):
     """dK and dV for the selected key rows only: ([len(keys), Hkv, d] x 2),
     from the query rows [q_lo, q_hi) (default: all rows; a smaller interval
     gives that interval's contribution, e.g. one ring or context-parallel
@@ -188,7 +225,15 @@ def attn_bwd_keys(q, k, v, do, keys, scale, s_valid=None, cu_seqlens=None, causa
     the keys needs LSE_i and D_i = dO_i . O_i over its WHOLE row, so those
     rows are run through attn_fwd_rows first; the gradient terms are then
     formed for the selected key columns only:
-        dK_j = scale sum_h sum_i P_ij (dP_ij - D_i) q_i,  dV_j = sum_h sum_i P_ij dO_i."""
+        dK_j = scale sum_h sum_i P_ij (dP_ij - D_i) q_i,  dV_j = sum_h sum_i P_ij dO_i.
+
+    with_abs: also return, per element, the sums of absolute values that
+    bound how far rounding the factors of these terms can move them (the
+    condition of each sum):
+        AdK_j = scale sum_h sum_i |q_i| (|dS_ij| + P_ij B_i),
+        AdV_j = sum_h sum_i P_ij |dO_i|,
+    with B_i = sum_e |dO_ie| (sum_l P_il |v_le|), the bound of D_i's own
+    sum. Returns (dK, dV, AdK, AdV)."""
     q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
     s, hq, hkv, d, g = _check(q, k, v)
     s_valid = s if s_valid is None else s_valid
@@ -197,18 +242,24 @@ def attn_bwd_keys(q, k, v, do, keys, scale, s_valid=None, cu_seqlens=None, causa
     keys = np.asarray(keys, dtype=np.int64)
     dk = np.zeros((len(keys), hkv, d))
     dv = np.zeros((len(keys), hkv, d))
+    adk = np.zeros((len(keys), hkv, d)) if with_abs else None
+    adv = np.zeros((len(keys), hkv, d)) if with_abs else None
+    out = (dk, dv, adk, adv) if with_abs else (dk, dv)
     # rows of the interval that see at least one selected key
     cand = np.arange(max(q_lo, int(keys.min()) if causal else q_lo), q_hi)
     if len(cand) == 0:
-        return dk, dv
+        return out
     seen = np.zeros(len(cand), dtype=bool)
     for r0 in range(0, len(cand), 4096):
         seen[r0:r0 + 4096] = _sees(cand[r0:r0 + 4096], keys, s_valid, doc, causal).any(axis=1)
     rows = cand[seen]
     if len(rows) == 0:
-        return dk, dv
-    o, lse = attn_fwd_rows(q, k, v, rows, scale, s_valid, cu_seqlens, causal)
+        return out
+    fw = attn_fwd_rows(q, k, v, rows, scale, s_valid, cu_seqlens, causal, with_abs=with_abs)
+    o, lse = fw[0], fw[1]
     dd = np.einsum("rhd,rhd->hr", do[rows], o)          # D_i = dO_i . O_i, [Hq, rows]
+    if with_abs:
+        bb = np.einsum("rhd,rhd->hr", np.abs(do[rows]), fw[2])   # B_i, [Hq, rows]
     for b0 in range(0, len(rows), ROW_BLOCK):
         rb = rows[b0:b0 + ROW_BLOCK]
         m = _sees(rb, keys, s_valid, doc, causal)          # [rows, keys]
@@ -220,7 +271,11 @@ def attn_bwd_keys(q, k, v, do, keys, scale, s_valid=None, cu_seqlens=None, causa
             ds = p * (dp - dd[h, b0:b0 + len(rb)][:, None])
             dk[:, kvh, :] += scale * (ds.T @ q[rb, h, :])
             dv[:, kvh, :] += p.T @ do[rb, h, :]
-    return dk, dv
+            if with_abs:
+                w_ = np.abs(ds) + p * bb[h, b0:b0 + len(rb)][:, None]
+                adk[:, kvh, :] += scale * (w_.T @ np.abs(q[rb, h, :]))
+                adv[:, kvh, :] += p.T @ np.abs(do[rb, h, :])
+    return out
 
 
 def _sees(rows, keys, s_valid, doc, causal):

@@ -87,3 +87,24 @@ def test_checker_one_step_exception_only_at_four_and_up():
     bad[2] += 2 * step[2]
     with pytest.raises(AssertionError):
         check_close("v", bad, r, "bf16")
+
+
+def test_checker_bound_widens_elements_not_the_tensor_bars():
+    """A per-element rounding bound lets single large-magnitude elements
+    differ by more than 2e-2, but a zeroed, rescaled or shifted tensor still
+    fails the magnitude-relative bars."""
+    from tests.gpu_helpers import rounding_bound
+    ref = _reference()["dK"]
+    abs_sum = 4.0 * np.abs(ref) + 0.5          # terms of mixed sign: larger than |ref|
+    bound = rounding_bound(ref, abs_sum, 2)
+    got = bf16_rne(ref)
+    i = np.unravel_index(np.argmax(np.where(np.abs(ref) < 3.9, np.abs(ref), 0)), ref.shape)
+    assert np.abs(ref[i]) > 1.0
+    got[i] += 0.03 * np.sign(ref[i])            # one element off by 0.03, inside its bound
+    assert bound[i] > 0.03
+    with pytest.raises(AssertionError):
+        check_close("dK", got, ref, "bf16")
+    check_close("dK", got, ref, "bf16", bound=bound)
+    for bad in (np.zeros_like(ref), 1.1 * ref, np.roll(ref, 1, axis=0)):
+        with pytest.raises(AssertionError):
+            check_close("dK", bf16_rne(bad), ref, "bf16", bound=bound)

@@ -222,6 +222,8 @@ def test_sampled_rows_and_keys_match_full():
         np.testing.assert_allclose(lse_r, lse[:, rows], atol=1e-13)
         dq_r = oracle.attn_bwd_rows(q, k, v, do, rows, 0.25, sv, cu_)
         np.testing.assert_allclose(dq_r, dq[rows], atol=1e-12)
+        dq_r = oracle.attn_bwd_rows(q, k, v, do, rows, 0.25, sv, cu_, lse=lse[:, rows])
+        np.testing.assert_allclose(dq_r, dq[rows], atol=1e-12)
         keys = np.array([5, 99, 100, 200, 259, 280, 296, 297, 299])
         dk_r, dv_r = oracle.attn_bwd_keys(q, k, v, do, keys, 0.25, sv, cu_)
         np.testing.assert_allclose(dk_r, dk[keys], atol=1e-12)
@@ -241,10 +243,10 @@ def test_planted_mistakes_are_caught(monkeypatch):
     orig = A._bwd_block
 
     def no_d(*args):
-        nc, p, ds = orig(*args)
+        c0, nc, p, ds = orig(*args)
         q_, k_, v_, do_, h, kvh, rb = args[:7]
-        dp = do_[rb, h, :] @ v_[:nc, kvh, :].T
-        return nc, p, p * dp  # D dropped
+        dp = do_[rb, h, :] @ v_[c0:nc, kvh, :].T
+        return c0, nc, p, p * dp  # D dropped
 
     monkeypatch.setattr(A, "_bwd_block", no_d)
     o, lse = oracle.attn_fwd(q, k, v, scale, s_valid, cu, causal)
@@ -279,3 +281,66 @@ def test_sampled_keys_of_a_query_interval_match_torch(case):
                                       q_lo=q_lo, q_hi=q_hi)
         np.testing.assert_allclose(dk, rdk[keys], atol=RTOL_LIB)
         np.testing.assert_allclose(dv, rdv[keys], atol=RTOL_LIB)
+
+
+def test_sampled_key_absolute_sums_by_brute_force():
+    """attn_bwd_keys(with_abs=True): the absolute-term sums written out with
+    explicit loops over rows, keys and heads from their definitions
+    (P from the textbook softmax, dS = P (dP - D), D = dO . O)."""
+    import math
+    s, hq, hkv, d = 12, 4, 2, 3
+    cu, s_valid, scale = [0, 5, 12], 11, 0.7
+    q, k, v, do = (rand((s, h, d), 140 + i) for i, h in enumerate((hq, hkv, hkv, hq)))
+    g = hq // hkv
+    doc = [0] * 5 + [1] * 7
+
+    def allowed(i, j):
+        return j < s_valid and j <= i and doc[i] == doc[j]
+
+    P = np.zeros((hq, s, s))
+    for h in range(hq):
+        for i in range(s):
+            zs = {j: scale * sum(q[i, h, e] * k[j, h // g, e] for e in range(d))
+                  for j in range(s) if allowed(i, j)}
+            tot = sum(math.exp(z) for z in zs.values())
+            for j, z in zs.items():
+                P[h, i, j] = math.exp(z) / tot
+    keys = np.array([0, 3, 5, 6, 10, 11])
+    want_dk = np.zeros((len(keys), hkv, d))
+    want_adk = np.zeros((len(keys), hkv, d))
+    want_adv = np.zeros((len(keys), hkv, d))
+    for h in range(hq):
+        for i in range(s):
+            o_i = [sum(P[h, i, l] * v[l, h // g, e] for l in range(s)) for e in range(d)]
+            oabs_i = [sum(P[h, i, l] * abs(v[l, h // g, e]) for l in range(s)) for e in range(d)]
+            D = sum(do[i, h, e] * o_i[e] for e in range(d))
+            B = sum(abs(do[i, h, e]) * oabs_i[e] for e in range(d))
+            for a, j in enumerate(keys):
+                if not allowed(i, j):
+                    continue
+                dp = sum(do[i, h, e] * v[j, h // g, e] for e in range(d))
+                ds = P[h, i, j] * (dp - D)
+                for e in range(d):
+                    want_dk[a, h // g, e] += scale * ds * q[i, h, e]
+                    want_adk[a, h // g, e] += scale * abs(q[i, h, e]) * (abs(ds) + P[h, i, j] * B)
+                    want_adv[a, h // g, e] += P[h, i, j] * abs(do[i, h, e])
+    dk, dv, adk, adv = oracle.attn_bwd_keys(q, k, v, do, keys, scale, s_valid, cu, True,
+                                            with_abs=True)
+    np.testing.assert_allclose(dk, want_dk, atol=1e-12)
+    np.testing.assert_allclose(adk, want_adk, atol=1e-12)
+    np.testing.assert_allclose(adv, want_adv, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_sampled_key_absolute_sums_bound_the_values(case):
+    """Triangle inequality: |dK| <= AdK and |dV| <= AdV element-wise; a key
+    seen by one row of one head (the last key of a causal MHA sequence) has
+    AdV = |dV| exactly."""
+    name, s, s_valid, hq, hkv, d, cu, causal = case
+    q, k, v, do = (rand((s, h, d), 150 + seed) for seed, h in zip(range(4), (hq, hkv, hkv, hq)))
+    keys = np.arange(s)
+    dk, dv, adk, adv = oracle.attn_bwd_keys(q, k, v, do, keys, 1.0 / np.sqrt(d), s_valid, cu,
+                                            causal, with_abs=True)
+    assert (np.abs(dk) <= adk + 1e-12).all() and (np.abs(dv) <= adv + 1e-12).all()
+    if name == "causal_mha":
+        np.testing.assert_allclose(adv[-1], np.abs(dv[-1]), rtol=1e-12)
