@@ -487,14 +487,14 @@ def main():
            for t in pk} for _ in range(n_sets)]
     reps = 20
 
-    def timed(fn):
+    def timed(fn, sets=n_sets):
         for i in range(3):
-            fn(i % n_sets)
+            fn(i % sets)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(reps):
-            fn(i % n_sets)
+            fn(i % sets)
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
@@ -505,10 +505,21 @@ def main():
 
     pack_ms = timed(pack_all)
     permute_gbs = nbytes / (pack_ms * 1e-3) / 1e9
+    # composite unpack of O: every rank's head-sharded O [P, s_pad, H/P, d]
+    # back to [S, H, d], padding rows dropped (bytes: S rows read, S written),
+    # rotated over enough sets to exceed 1 GiB like the pack
+    hq_full = full[workloads.Q].shape[1]
+    ubytes = 2 * w.s * hq_full * d * 2
+    u_sets = max(1, -(-(1 << 30) // ubytes))
+    uin = [ys[0][workloads.Q].clone() for _ in range(u_sets)]
+    del srcs, ys
+    uout = [torch.empty((w.s, hq_full, d), dtype=torch.bfloat16, device=dev) for _ in range(u_sets)]
+    unpack_ms = timed(lambda i: usp.usp_unpack_head2seq(uin[i], w.s, out=uout[i]), u_sets)
+    unpack_gbs = ubytes / (unpack_ms * 1e-3) / 1e9
+    del uin, uout
     # reference copy on the same box: torch's device-to-device copy (the
     # runtime's blit kernel) reading and writing the same total number of
     # bytes, rotated the same way
-    del srcs, ys
     cin = [torch.empty(nbytes // 2, dtype=torch.uint8, device=dev).fill_(1) for _ in range(n_sets)]
     cout = [torch.empty_like(x) for x in cin]
     copy_ms = timed(lambda i: cout[i].copy_(cin[i]))
@@ -555,6 +566,10 @@ def main():
         "permute_frac_of_hbm_peak": round(permute_gbs / PEAK_HBM_GBS, 4),
         "permute_bytes": nbytes,
         "permute_buffer_sets": n_sets,
+        "unpack_gbps": round(unpack_gbs, 1),
+        "unpack_frac_of_hbm_peak": round(unpack_gbs / PEAK_HBM_GBS, 4),
+        "unpack_bytes": ubytes,
+        "unpack_buffer_sets": u_sets,
         "d2d_memcpy_gbps": round(copy_gbs, 1),
         "permute_over_d2d_memcpy": round(permute_gbs / copy_gbs, 4),
         "kernels_ms_per_step": {e["name"]: round(e["total_ms"] / args.steps, 4) for e in trace},

@@ -1,17 +1,18 @@
 """GPU parity of usp_attn_fwd / usp_attn_bwd against the fp64 oracle.
 
-Small problems (several tiles plus a ragged tail) are compared element by
-element over every output; the full-size workloads are compared on sampled
-query rows (O, LSE, dQ), on key rows near the end of the sequence or of each
-document (dK, dV: few query rows see them, so the oracle computes them
-exactly), and through identities that hold at any size."""
+Small problems (several tiles plus a ragged tail) and an 8K-token problem on
+every kernel's long-sequence path are compared element by element over every
+output; the full-size workloads are compared on sampled query rows (O, LSE,
+dQ), on the same sample as key rows (dK, dV, against oracle values stored by
+tests/golden/make_full_size_keys.py), and through identities that hold at
+any size."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads
-from tests.gpu_helpers import check_close, f64, gpu, say
+from tests.gpu_helpers import check_close, f64, gpu, rounding_bound, say
 
 pytestmark = pytest.mark.gpu
 
@@ -183,27 +184,111 @@ def from_bits(a):
 
 
 def share_inputs(w, dev):
-    """Full-model tensors -> GPU pack -> rank-0 share (GPU), and the oracle's
-    own pack of the same seeded tensors (CPU, fp64)."""
+    """Full-model tensors -> GPU pack -> rank-0 share (GPU), the oracle's own
+    pack of the same seeded tensors (CPU, fp64), and a SHA-256 of the
+    oracle-packed bf16 bits (which the stored key samples record)."""
     L = usp()
-    gpu_in, ref_in = [], []
+    gpu_in, ref_in, ref_bits = [], [], []
     for t in (workloads.Q, workloads.K, workloads.V, workloads.DO):
         x = workloads.tensor(w, t)
         y = L.usp_pad_pack_seq2head(x.to(dev), w.p)
         gpu_in.append(y[0].contiguous())
         del y
-        ref_in.append(from_bits(oracle.pad_pack_seq2head(bits(x), w.p)[0]).double().numpy())
+        b = oracle.pad_pack_seq2head(bits(x), w.p)[0]
+        ref_bits.append(b)
+        ref_in.append(from_bits(b).double().numpy())
         del x
     torch.cuda.synchronize()
-    return gpu_in, ref_in
+    return gpu_in, ref_in, input_sha256(ref_bits)
 
 
-def tail_keys(w, cu):
-    ends = [w.s_pad] if cu is None else list(cu[1:])
-    keys = set()
-    for e in ends:
-        keys.update(range(max(0, e - 24), e))
-    return np.array(sorted(keys), dtype=np.int64)
+def oracle_by_group(q64, k64, v64, do64, scale, s_valid, cu, causal):
+    """Full oracle forward + backward, one KV-head group at a time (the
+    groups are independent problems), the groups in parallel threads, each
+    with a single-threaded BLAS (nested BLAS threads oversubscribe the host
+    many times over)."""
+    import concurrent.futures as cf
+
+    from threadpoolctl import threadpool_limits
+    hq, hkv = q64.shape[1], k64.shape[1]
+    g = hq // hkv
+
+    def one(j):
+        qs, ks = slice(g * j, g * (j + 1)), slice(j, j + 1)
+        o, lse = oracle.attn_fwd(q64[:, qs], k64[:, ks], v64[:, ks], scale, s_valid, cu, causal)
+        dq, dk, dv = oracle.attn_bwd(q64[:, qs], k64[:, ks], v64[:, ks], o, lse, do64[:, qs],
+                                     scale, s_valid, cu, causal)
+        return o, lse, dq, dk, dv
+
+    with threadpool_limits(1), cf.ThreadPoolExecutor(min(hkv, 16)) as ex:
+        parts = list(ex.map(one, range(hkv)))
+    cat = [np.concatenate([p[i] for p in parts], axis=1 if i != 1 else 0) for i in range(5)]
+    return cat
+
+
+# Every kernel on its long-sequence path: 32 Q / 8 KV heads (the 8K workload's
+# full model on one GPU), d = 128, 8192 tokens. The dK/dV grid then has 512
+# blocks of 128 keys (one row chunk: the direct-store epilogue of the 120K
+# step), the forward 1024 workgroups and dQ 2048 (one pass each, no key
+# splits), so no reduction or merge kernel runs. Compared element by element.
+LONG = [
+    # name, S, s_valid, cu_seqlens, causal, d
+    ("long_8k_32q8kv", 8192, 8192, None, True, 128),
+    ("long_8k_32q8kv_padded", 8192, 8190, None, True, 128),
+    ("long_8k_32q8kv_docs", 8192, 8192, [0, 1000, 1001, 5000, 8192], True, 128),
+]
+SINGLE_PASS = {"attn_fwd_kmajor_v", "attn_fwd_bf16", "attn_bwd_rowdot_bf16",
+               "attn_bwd_dkdv_bf16", "attn_bwd_dq_bf16"}
+
+
+@pytest.mark.parametrize("case", LONG, ids=[c[0] for c in LONG])
+def test_bf16_long_path_full_compare(case):
+    name, s, s_valid, cu, causal, d = case
+    hq, hkv = 32, 8
+    L = usp()
+    dev = gpu()
+    say(f"bf16 {name}: S={s} s_valid={s_valid} hq={hq} hkv={hkv} d={d}")
+    assert L.usp_attn_fwd_num_splits(s, s, hq, hkv, d, L.USP_BF16, s_k_valid=s_valid) == 1
+    assert L.usp_attn_bwd_num_splits(s, s, hq, hkv, d, L.USP_BF16, s_k_valid=s_valid) == 1
+    q, k, v, do = (seeded((s, h, d), 5000 + i, torch.bfloat16)
+                   for i, h in enumerate((hq, hkv, hkv, hq)))
+    if s_valid < s:
+        for t in (q, k, v, do):
+            t[s_valid:] = 0
+    L.usp_trace_collect()
+    L.usp_trace_enable(True)
+    try:
+        got = run_pair(q, k, v, do, s_valid, cu, causal, dev)
+        ran = {e["name"] for e in L.usp_trace_collect()}
+    finally:
+        L.usp_trace_enable(False)
+    assert ran == SINGLE_PASS, ran
+    say(f"  oracle, {hkv} groups in parallel")
+    o, lse, dq, dk, dv = oracle_by_group(*(f64(t) for t in (q, k, v, do)), d ** -0.5, s_valid, cu,
+                                          causal)
+    check_close("O", f64(got["o"]), o, "bf16")
+    check_close("LSE", f64(got["lse"]), lse, "bf16")
+    check_close("dQ", f64(got["dq"]), dq, "bf16")
+    check_close("dK", f64(got["dk"]), dk, "bf16")
+    check_close("dV", f64(got["dv"]), dv, "bf16")
+
+
+def key_fixture(name):
+    """Stored oracle dK / dV on the full-size key sample (written by
+    tests/golden/make_full_size_keys.py from the oracle alone)."""
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "full_size_keys",
+                        f"{name}.npz")
+    with np.load(path, allow_pickle=False) as z:
+        return {k: z[k] for k in z.files}
+
+
+def input_sha256(arrays_bits):
+    import hashlib
+    h = hashlib.sha256()
+    for a in arrays_bits:
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
 
 
 @pytest.mark.parametrize("name", ["s8k", "s32k", "s120k", "s120k_pad", "thd131k"])
@@ -213,7 +298,7 @@ def test_workload(name):
     w = workloads.WORKLOADS[name]
     cu = workloads.cu_seqlens(workloads.doc_lengths(w.s)).tolist() if w.thd else None
     say(f"{name}: generating + packing S={w.s} (s_pad={w.s_pad}) hq={w.hq} hkv={w.hkv}")
-    (q, k, v, do), (q64, k64, v64, do64) = share_inputs(w, dev)
+    (q, k, v, do), (q64, k64, v64, do64), sha = share_inputs(w, dev)
     say(f"{name}: forward")
     o, lse = L.usp_attn_fwd(q, k, v, s_valid=w.s, cu_seqlens=cu)
     torch.cuda.synchronize()
@@ -222,9 +307,7 @@ def test_workload(name):
         dq, dk, dv = L.usp_attn_bwd(q, k, v, o, lse, do, s_valid=w.s, cu_seqlens=cu)
         torch.cuda.synchronize()
     scale = w.scale
-    slice_edges = [r * (w.s_pad // w.p) for r in range(1, w.p)]
-    rows = workloads.row_sample(w, n_uniform=160, edge=16,
-                                boundaries=slice_edges + (cu[1:-1] if cu else []))
+    rows = workloads.row_sample(w)
     say(f"{name}: oracle on {len(rows)} sampled rows")
     o_ref, lse_ref = oracle.attn_fwd_rows(q64, k64, v64, rows, scale, w.s, cu)
     check_close("O[rows]", f64(o)[rows], o_ref, "bf16")
@@ -232,14 +315,19 @@ def test_workload(name):
     assert np.isfinite(f64(o)).all() and np.isfinite(f64(lse)).all()
     if not w.backward:
         return
-    dq_ref = oracle.attn_bwd_rows(q64, k64, v64, do64, rows, scale, w.s, cu)
+    dq_ref = oracle.attn_bwd_rows(q64, k64, v64, do64, rows, scale, w.s, cu, lse=lse_ref)
     check_close("dQ[rows]", f64(dq)[rows], dq_ref, "bf16")
-    keys = tail_keys(w, cu)
-    say(f"{name}: oracle dK/dV on {len(keys)} tail keys")
-    dk_ref, dv_ref = oracle.attn_bwd_keys(q64, k64, v64, do64, keys, scale, w.s, cu)
+    # dK / dV on the same sample as keys, against the stored oracle values
+    fx = key_fixture(name)
+    assert str(fx["inputs_sha256"]) == sha, "stored key sample was made from other inputs"
+    keys = fx["keys"]
+    np.testing.assert_array_equal(keys, rows)
     dk64, dv64, do_all = f64(dk), f64(dv), do64
-    check_close("dK[keys]", dk64[keys], dk_ref, "bf16")
-    check_close("dV[keys]", dv64[keys], dv_ref, "bf16")
+    say(f"{name}: dK/dV on {len(keys)} sampled keys")
+    check_close("dK[keys]", dk64[keys], fx["dk"].astype(np.float64), "bf16",
+                bound=rounding_bound(fx["dk"], fx["adk"], 2))
+    check_close("dV[keys]", dv64[keys], fx["dv"].astype(np.float64), "bf16",
+                bound=rounding_bound(fx["dv"], fx["adv"], 1))
     for a in (f64(dq), dk64, dv64):
         assert np.isfinite(a).all()
     # identities over the full outputs, per document: sum_j dK_j = 0 and

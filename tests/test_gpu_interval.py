@@ -15,7 +15,8 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_helpers import check_close, f64, gpu, say
+from tests.gpu_helpers import check_close, f64, gpu, rounding_bound, say
+from tests.test_gpu_attention import bits, input_sha256, key_fixture
 
 pytestmark = pytest.mark.gpu
 
@@ -338,9 +339,9 @@ def test_bf16_usp_ulysses2_ring4_last_rank_120k():
     """One GPU's share of USP on 8 GPUs as Ulysses 2 x Ring 4 at S = 120000:
     the heads of Ulysses group 0 (16 Q / 4 KV), the last ring rank's 30000
     query rows against the four key blocks in ring order. Merged O / LSE and
-    the accumulated dQ on sampled rows, and dK / dV of the sequence's last
-    keys (seen only by this rank's rows), against the oracle's full-sequence
-    attention."""
+    the accumulated dQ on sampled rows of the rank, and dK / dV on keys
+    sampled over the whole sequence (this rank's rows' contributions, stored
+    by tests/golden/make_full_size_keys.py), against the oracle."""
     L = usp()
     dev = gpu()
     w = workloads.WORKLOADS["s120k"]
@@ -375,19 +376,27 @@ def test_bf16_usp_ulysses2_ring4_last_rank_120k():
                                 k_off=ka, softmax_scale=w.scale, accumulate=True, dq=dq,
                                 dk=dk[ka:kb], dv=dv[ka:kb])
     torch.cuda.synchronize()
-    g = np.random.default_rng([w.cfg, 7, 9])
-    rows = np.unique(np.concatenate([np.arange(qa, qa + 8), np.arange(qb - 8, qb),
-                                     g.integers(qa, qb, size=48)]))
+    # rows: the rank's first and last 64 and 256 seeded uniform rows (each
+    # costs the oracle a full 16-head row); keys: the full-size sample over the
+    # whole sequence, against stored oracle values of this rank's rows'
+    # contributions
+    rows = workloads.index_sample(s, [w.cfg, 7, 9], 256, 64, [], lo=qa)
     q64, k64, v64, do64 = (f64(x[t]) for t in (workloads.Q, workloads.K, workloads.V, workloads.DO))
     say(f"  oracle on {len(rows)} rows")
     o_ref, lse_ref = oracle.attn_fwd_rows(q64, k64, v64, rows, w.scale)
     check_close("USP O[rows]", f64(acc_o)[rows - qa], o_ref, "bf16", bf16_out=False)
     check_close("USP LSE[rows]", f64(acc_l)[:, rows - qa], lse_ref, "bf16")
-    dq_ref = oracle.attn_bwd_rows(q64, k64, v64, do64, rows, w.scale)
+    dq_ref = oracle.attn_bwd_rows(q64, k64, v64, do64, rows, w.scale, lse=lse_ref)
     check_close("USP dQ[rows]", f64(dq)[rows - qa], dq_ref, "bf16", bf16_out=False)
-    keys = np.arange(s - 24, s)
-    dk_ref, dv_ref = oracle.attn_bwd_keys(q64, k64, v64, do64, keys, w.scale)
-    check_close("USP dK[tail]", f64(dk)[keys], dk_ref, "bf16", bf16_out=False)
-    check_close("USP dV[tail]", f64(dv)[keys], dv_ref, "bf16", bf16_out=False)
+    fx = key_fixture("usp_u2r4_120k")
+    assert str(fx["inputs_sha256"]) == input_sha256([bits(x[t]) for t in (
+        workloads.Q, workloads.K, workloads.V, workloads.DO)]), "stored keys made from other inputs"
+    assert int(fx["q_lo"]) == qa and int(fx["q_hi"]) == qb
+    keys = fx["keys"]
+    say(f"  dK/dV on {len(keys)} sampled keys")
+    check_close("USP dK[keys]", f64(dk)[keys], fx["dk"].astype(np.float64), "bf16", bf16_out=False,
+                bound=rounding_bound(fx["dk"], fx["adk"], 2, bf16_output=False))
+    check_close("USP dV[keys]", f64(dv)[keys], fx["dv"].astype(np.float64), "bf16", bf16_out=False,
+                bound=rounding_bound(fx["dv"], fx["adv"], 1, bf16_output=False))
     # keys of the first block are seen by every one of this rank's rows: finite, nonzero
     assert torch.isfinite(dk).all() and torch.isfinite(dv).all() and dk[:blk].abs().sum() > 0
