@@ -19,7 +19,8 @@
  * Conventions for every call:
  *   - All tensor pointers are DEVICE memory owned by the caller; the library
  *     never allocates device memory and keeps no state between calls (apart
- *     from the optional kernel trace below).
+ *     from the optional kernel trace below and the static workspace array of
+ *     usp_attn_bwd_noalloc).
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *     void*; NULL means the default stream). The return value is known
  *     synchronously: argument checks run on the host before any HIP call, so a
@@ -165,6 +166,38 @@ int usp_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                  int64_t s_pad, int64_t s_valid, const int32_t* cu_seqlens, int n_docs,
                  int hq, int hkv, int d, float softmax_scale, int causal, int dtype,
                  void* stream);
+
+/* Size of the library-owned backward workspace of usp_attn_bwd_noalloc, per
+ * GPU: 32 MiB. */
+#define USP_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * usp_attn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation. Same computation, kernels, arguments, outputs and
+ * errors as usp_attn_bwd; the workspace is a library-owned array of
+ * USP_NOALLOC_SCRATCH_BYTES in device memory, one per GPU, which each GPU the
+ * call runs on holds until the process ends. The call allocates nothing
+ * (no hipMalloc, no allocating library routine).
+ *   - The array of the CURRENT device is used: stream must belong to it.
+ *   - Calls on one GPU share its array. Calls that may overlap in time on one
+ *     GPU (different streams without ordering between them) race on it and
+ *     must not be issued; calls ordered on one stream are fine. Each call
+ *     rewrites every part of the array it reads, so nothing carries over from
+ *     the previous call and nothing needs clearing.
+ *   - Sizes whose required workspace (usp_attn_bwd's minimum: fp32 D and LSE
+ *     per query row and head, plus the dK/dV row-chunk partials of short
+ *     sequences) exceeds USP_NOALLOC_SCRATCH_BYTES return USP_ERR_WORKSPACE
+ *     before any device work: for example 120,000 rows with 4 query heads
+ *     need 3.8 MB and 131,072 rows with 16 heads 16.8 MB, but 8,192 rows on
+ *     one KV head (16 row chunks, 134 MB) are rejected. Room left in the array
+ *     goes to dQ key splits as in usp_attn_bwd.
+ */
+int usp_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         int64_t s_pad, int64_t s_valid, const int32_t* cu_seqlens, int n_docs,
+                         int hq, int hkv, int d, float softmax_scale, int causal, int dtype,
+                         void* stream);
 
 /*
  * Attention between a query interval and a key interval on global positions:

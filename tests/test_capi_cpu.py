@@ -51,7 +51,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.usp_version() == 110
+    assert L.usp_version() == 120
     for s in (OK, INVALID, UNSUPPORTED, NULLP, HIPERR, WORKSPACE, 12345):
         assert isinstance(L.usp_status_string(s), bytes)
     assert L.usp_status_string(0) == b"ok"
@@ -405,3 +405,41 @@ int main() {
                    capture_output=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout
+
+
+def bwd_na(L, s_pad=256, s_valid=256, cu=None, n_docs=0, hq=4, hkv=1, d=128, scale=0.088,
+           causal=1, dt=BF16, ptrs=None):
+    ptrs = ptrs or [A + (i << 26) for i in range(9)]
+    return L.usp_attn_bwd_noalloc(*(ctypes.c_void_p(x) for x in ptrs), s_pad, s_valid,
+                                  ctypes.c_void_p(cu), n_docs, hq, hkv, d, scale, causal, dt, None)
+
+
+def test_noalloc_backward_rejects_on_the_host(L):
+    """usp_attn_bwd_noalloc: the argument errors of usp_attn_bwd, and sizes
+    whose required workspace exceeds the static array, all before any HIP call."""
+    import ulysses_sequence_parallelism_amd as usp
+    assert usp.USP_NOALLOC_SCRATCH_BYTES == 32 << 20
+    text = open(HEADER).read()
+    assert re.search(r"#define USP_NOALLOC_SCRATCH_BYTES \(32u << 20\)", text)
+    assert bwd_na(L, s_valid=0) == INVALID
+    assert bwd_na(L, s_valid=257) == INVALID
+    assert bwd_na(L, hq=6, hkv=4) == INVALID
+    assert bwd_na(L, d=96) == UNSUPPORTED
+    assert bwd_na(L, dt=7) == UNSUPPORTED
+    assert bwd_na(L, scale=0.0) == INVALID
+    p = [A + (i << 26) for i in range(9)]
+    p[3] = 0
+    assert bwd_na(L, ptrs=p) == NULLP
+    p = [A + (i << 26) for i in range(9)]
+    p[7] = p[1]  # dk aliases k
+    assert bwd_na(L, ptrs=p) == INVALID
+    p[7] = A + (7 << 26) + 8  # misaligned
+    assert bwd_na(L, ptrs=p) == INVALID
+    # required workspace beyond 32 MiB: 8192 rows on one KV head need 16 row
+    # chunks of fp32 partial dK and dV (134 MB)
+    need = L.usp_attn_bwd_workspace_bytes(8192, 4, 1, 128, BF16)
+    assert need > (32 << 20)
+    assert bwd_na(L, s_pad=8192, s_valid=8192) == WORKSPACE
+    # D and LSE alone: 2^19 rows x 16 heads x 8 bytes = 64 MiB
+    far = [A + (i << 32) for i in range(9)]
+    assert bwd_na(L, s_pad=1 << 19, s_valid=1 << 19, hq=16, hkv=16, ptrs=far) == WORKSPACE

@@ -29,6 +29,8 @@ __all__ = [
     "usp_attn_fwd",
     "usp_attn_bwd_workspace_bytes",
     "usp_attn_bwd",
+    "usp_attn_bwd_noalloc",
+    "USP_NOALLOC_SCRATCH_BYTES",
     "usp_attn_fwd_interval",
     "usp_attn_fwd_num_splits",
     "usp_attn_bwd_num_splits",
@@ -43,6 +45,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libusp.so")
 USP_BF16, USP_FP32 = 0, 1
+USP_NOALLOC_SCRATCH_BYTES = 32 << 20   # include/usp.h
 _DTYPES = {torch.bfloat16: USP_BF16, torch.float32: USP_FP32}
 
 _lib = None
@@ -94,6 +97,9 @@ def lib() -> ctypes.CDLL:
         L.usp_attn_bwd.restype = i32
         L.usp_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, vp, i32,
                                    i32, i32, i32, f32, i32, i32, vp]
+        L.usp_attn_bwd_noalloc.restype = i32
+        L.usp_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, i32,
+                                           i32, i32, i32, f32, i32, i32, vp]
         L.usp_attn_fwd_interval.restype = i32
         L.usp_attn_fwd_interval.argtypes = [vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64,
                                             vp, i32, i32, i32, i32, f32, i32, i32, i32, vp]
@@ -314,6 +320,40 @@ def usp_attn_bwd(q, k, v, o, lse, dout, s_valid=None, cu_seqlens=None, causal=Tr
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), s_pad, s_valid, _ptr(cu),
         n_docs, hq, hkv, d, scale, int(causal), dt, _stream(stream)))
+    return dq, dk, dv
+
+
+def usp_attn_bwd_noalloc(q, k, v, o, lse, dout, s_valid=None, cu_seqlens=None, causal=True,
+                         softmax_scale=None, dq=None, dk=None, dv=None, stream=None):
+    """usp_attn_bwd with the library's own static workspace (see usp.h): the
+    library allocates nothing. Pass dq, dk, dv to allocate nothing here either
+    (cu_seqlens, if given, should then be a device int32 tensor). Returns
+    (dq, dk, dv)."""
+    _contig(q, k, v, o, lse, dout)
+    s_pad, hq, d = q.shape
+    hkv = k.shape[1]
+    s_valid = s_pad if s_valid is None else s_valid
+    scale = float(d) ** -0.5 if softmax_scale is None else softmax_scale
+    dt = _dtype(q)
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.ndim != 1 or not cu_seqlens.is_contiguous():
+            raise UspError("cu_seqlens", -1)
+        cu, n_docs = cu_seqlens, cu_seqlens.numel() - 1
+    else:
+        cu, n_docs = _cu(cu_seqlens, s_pad, q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _contig(dq, dk, dv)
+    kshape = (s_pad, hkv, d)
+    _shapes("usp_attn_bwd_noalloc", k=(k, kshape), v=(v, kshape), o=(o, q.shape),
+            dout=(dout, q.shape), lse=(lse, (hq, s_pad)), dq=(dq, q.shape), dk=(dk, kshape),
+            dv=(dv, kshape))
+    _same_dtype("usp_attn_bwd_noalloc", q.dtype, k=k, v=v, o=o, dout=dout, dq=dq, dk=dk, dv=dv)
+    _same_dtype("usp_attn_bwd_noalloc", torch.float32, lse=lse)
+    _check("usp_attn_bwd_noalloc", lib().usp_attn_bwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        s_pad, s_valid, _ptr(cu), n_docs, hq, hkv, d, scale, int(causal), dt, _stream(stream)))
     return dq, dk, dv
 
 

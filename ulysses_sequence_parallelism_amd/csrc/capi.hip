@@ -4,12 +4,14 @@
 // machine without a GPU).
 #include <math.h>
 
+#include <mutex>
+
 #include "usp_common.h"
 #include "usp_internal.h"
 
 namespace {
 
-constexpr int kAbiVersion = 110;
+constexpr int kAbiVersion = 120;
 
 size_t elem_bytes(int dtype) { return dtype == USP_BF16 ? 2 : 4; }
 
@@ -127,11 +129,17 @@ int fwd_checked(const void* q, const void* k, const void* v, void* o, float* lse
   return dtype == USP_BF16 ? usp::attn_fwd_bf16(a) : usp::attn_fwd_f32(a);
 }
 
-int bwd_checked(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                const void* dout, void* dq, void* dk, void* dv, void* workspace,
-                size_t workspace_bytes, int64_t s_q, int64_t q_off, int64_t s_k, int64_t k_off,
-                int64_t s_k_valid, const int32_t* cu, int n_docs, int hq, int hkv, int d,
-                float scale, int causal, int dtype, int grad_dtype, int accumulate, void* stream) {
+// Every check of a backward call that does not involve the workspace; on
+// success *need holds the workspace bytes the call requires and *spans the
+// caller's input and output ranges.
+struct BwdSpans {
+  Span ins[6], outs[3];
+};
+
+int bwd_validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, int64_t s_q, int64_t s_k,
+                 const int32_t* cu, int hq, int hkv, int d, int dtype, int grad_dtype,
+                 int accumulate, size_t* need, BwdSpans* sp) {
   if (grad_dtype != USP_BF16 && grad_dtype != USP_FP32) return USP_ERR_UNSUPPORTED;
   if (dtype == USP_FP32 && grad_dtype != USP_FP32) return USP_ERR_UNSUPPORTED;
   if (accumulate != 0 && accumulate != 1) return USP_ERR_INVALID;
@@ -145,22 +153,27 @@ int bwd_checked(const void* q, const void* k, const void* v, const void* o, cons
   const size_t qb = (size_t)s_q * hq * d * es, kb = (size_t)s_k * hkv * d * es;
   const size_t gqb = (size_t)s_q * hq * d * gs, gkb = (size_t)s_k * hkv * d * gs;
   const size_t lb = (size_t)s_q * hq * sizeof(float);
+  *sp = BwdSpans{{{q, qb}, {k, kb}, {v, kb}, {o, qb}, {lse, lb}, {dout, qb}},
+                 {{dq, gqb}, {dk, gkb}, {dv, gkb}}};
+  for (const Span& a : sp->outs)
+    for (const Span& b : sp->ins)
+      if (overlap(a, b)) return USP_ERR_INVALID;
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(sp->outs[i], sp->outs[j])) return USP_ERR_INVALID;
   // bf16: room beyond the required part (as much as the workspace query
   // returns) lets a short call split dQ's keys
-  const size_t need = dtype == USP_BF16
-                          ? usp::attn_bwd_bf16_min_workspace(s_q, s_k, hq, hkv, d)
-                          : usp_attn_bwd_interval_workspace_bytes(s_q, s_k, hq, hkv, d, dtype);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return USP_ERR_WORKSPACE;
-  if (need > 0 && !aligned16(workspace)) return USP_ERR_INVALID;
-  const size_t used = dtype == USP_BF16 ? workspace_bytes : need;
-  const Span ins[] = {{q, qb}, {k, kb}, {v, kb}, {o, qb}, {lse, lb}, {dout, qb}};
-  const Span outs[] = {{dq, gqb}, {dk, gkb}, {dv, gkb}, {workspace, need > 0 ? used : 0}};
-  for (const Span& a : outs)
-    for (const Span& b : ins)
-      if (overlap(a, b)) return USP_ERR_INVALID;
-  for (int i = 0; i < 4; ++i)
-    for (int j = i + 1; j < 4; ++j)
-      if (overlap(outs[i], outs[j])) return USP_ERR_INVALID;
+  *need = dtype == USP_BF16 ? usp::attn_bwd_bf16_min_workspace(s_q, s_k, hq, hkv, d)
+                            : usp_attn_bwd_interval_workspace_bytes(s_q, s_k, hq, hkv, d, dtype);
+  return USP_OK;
+}
+
+int bwd_dispatch(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, int64_t s_q, int64_t q_off, int64_t s_k, int64_t k_off,
+                 int64_t s_k_valid, const int32_t* cu, int n_docs, int hq, int hkv, int d,
+                 float scale, int causal, int dtype, int grad_dtype, int accumulate,
+                 void* stream) {
   usp::AttnArgs a = interval_args(s_q, q_off, s_k, k_off, s_k_valid, cu, n_docs, hq, hkv, d,
                                   scale, causal, stream);
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
@@ -168,6 +181,54 @@ int bwd_checked(const void* q, const void* k, const void* v, const void* o, cons
   a.out_f32 = grad_dtype == USP_FP32;
   a.accumulate = accumulate;
   return dtype == USP_BF16 ? usp::attn_bwd_bf16(a) : usp::attn_bwd_f32(a);
+}
+
+int bwd_checked(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, int64_t s_q, int64_t q_off, int64_t s_k, int64_t k_off,
+                int64_t s_k_valid, const int32_t* cu, int n_docs, int hq, int hkv, int d,
+                float scale, int causal, int dtype, int grad_dtype, int accumulate, void* stream) {
+  size_t need = 0;
+  BwdSpans sp;
+  int rc = bwd_validate(q, k, v, o, lse, dout, dq, dk, dv, s_q, s_k, cu, hq, hkv, d, dtype,
+                        grad_dtype, accumulate, &need, &sp);
+  if (rc != USP_OK) return rc;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return USP_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return USP_ERR_INVALID;
+  const Span ws{workspace, need > 0 ? (dtype == USP_BF16 ? workspace_bytes : need) : 0};
+  for (const Span& b : sp.ins)
+    if (overlap(ws, b)) return USP_ERR_INVALID;
+  for (const Span& b : sp.outs)
+    if (overlap(ws, b)) return USP_ERR_INVALID;
+  return bwd_dispatch(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, s_q, q_off,
+                      s_k, k_off, s_k_valid, cu, n_docs, hq, hkv, d, scale, causal, dtype,
+                      grad_dtype, accumulate, stream);
+}
+
+// The backward workspace of usp_attn_bwd_noalloc: a library-owned array in
+// device memory, one per GPU (each device that loads the library's code
+// object holds its own copy at its own address), kept until the process ends.
+// In host code `scratch` only names the symbol: its device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[USP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's scratch array (looked up on first use).
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return USP_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return USP_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return USP_OK;
 }
 
 }  // namespace
@@ -260,6 +321,28 @@ int usp_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
   return bwd_checked(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, s_pad, 0,
                      s_pad, 0, s_valid, cu_seqlens, n_docs, hq, hkv, d, softmax_scale, causal,
                      dtype, dtype, 0, stream);
+}
+
+int usp_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         int64_t s_pad, int64_t s_valid, const int32_t* cu_seqlens, int n_docs,
+                         int hq, int hkv, int d, float softmax_scale, int causal, int dtype,
+                         void* stream) {
+  int rc = check_attn(s_pad, s_valid, cu_seqlens, n_docs, hq, hkv, d, softmax_scale, causal, dtype);
+  if (rc != USP_OK) return rc;
+  size_t need = 0;
+  BwdSpans sp;
+  rc = bwd_validate(q, k, v, o, lse, dout, dq, dk, dv, s_pad, s_pad, cu_seqlens, hq, hkv, d, dtype,
+                    dtype, 0, &need, &sp);
+  if (rc != USP_OK) return rc;
+  if (need > (size_t)USP_NOALLOC_SCRATCH_BYTES) return USP_ERR_WORKSPACE;
+  // the first HIP call: every argument check has passed
+  void* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc != USP_OK) return rc;
+  return bwd_dispatch(q, k, v, o, lse, dout, dq, dk, dv, ws, USP_NOALLOC_SCRATCH_BYTES, s_pad, 0,
+                      s_pad, 0, s_valid, cu_seqlens, n_docs, hq, hkv, d, softmax_scale, causal,
+                      dtype, dtype, 0, stream);
 }
 
 int usp_attn_fwd_interval(const void* q, const void* k, const void* v, void* o, float* lse,
