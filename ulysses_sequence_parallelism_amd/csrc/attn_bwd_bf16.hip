@@ -611,12 +611,30 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
   // wave-uniform base plus a 32-bit lane offset.
   const int wu = __builtin_amdgcn_readfirstlane(w);  // LDS destinations go to M0
   const uint32_t key_bytes = (uint32_t)pr.hkv * D * 2;
+  const int q_in_part = lane / KC;  // key within a part; lane % KC is the LDS slot
+  // lane offsets of the parts of a tile that lies inside the sequence (a
+  // constant per lane: key q_in_part of the part, swizzled chunk)
+  uint32_t kvoff[PPW];
+#pragma unroll
+  for (int j = 0; j < PPW; ++j)
+    kvoff[j] = (uint32_t)q_in_part * key_bytes +
+               ((uint32_t)((lane % KC) ^ swz_row<D>(RPP * (PPW * wu + j) + q_in_part)) << 4);
   auto load_tile = [&](int t0, int buf) {
     const uint32_t dk = lds_addr(&lkv[buf][0]);
     const uint32_t dv = lds_addr(&lkv[2 + buf][0]);
     const char* kb = reinterpret_cast<const char*>(pr.k) + (int64_t)kvh * (D * 2);
     const char* vb = reinterpret_cast<const char*>(pr.v) + (int64_t)kvh * (D * 2);
-    const int q = lane / KC;  // key within the part; lane % KC is the LDS slot
+    if (t0 + BN <= s_k) {
+#pragma unroll
+      for (int j = 0; j < PPW; ++j) {
+        const int part = PPW * wu + j;
+        const int64_t row = (int64_t)(t0 + RPP * part) * key_bytes;
+        lds_dma16(kb + row, kvoff[j], dk + part * 1024);
+        lds_dma16(vb + row, kvoff[j], dv + part * 1024);
+      }
+      return;
+    }
+    const int q = q_in_part;
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
       const int part = PPW * wu + j;
