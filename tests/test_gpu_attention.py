@@ -51,6 +51,10 @@ SMALL = [
     ("docs", 2100, 2100, 4, 1, [0, 100, 101, 1000, 1377, 2100], True),
     ("docs_16q4kv", 2048, 2048, 16, 4, [0, 700, 1300, 2048], True),
     ("bidirectional_padded", 500, 490, 4, 1, None, False),
+    # no padding, length not a multiple of the 128-key block: the last block's
+    # tail keys lie past the sequence end without being padding keys
+    ("bidirectional_ragged", 500, 500, 4, 1, None, False),
+    ("d64_bidirectional_ragged_gqa8", 2500, 2500, 8, 1, None, False, 64),
     ("bidirectional_docs", 600, 600, 4, 2, [0, 250, 600], False),
     # shorter than one 32-row block: every tile is a ragged tail
     ("tiny_1", 1, 1, 4, 1, None, True),
