@@ -135,9 +135,10 @@ int usp_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  void* stream);
 
 /* Workspace bytes usp_attn_bwd needs for these sizes: per (query head, row)
- * fp32 D and LSE values and, for bf16 on short sequences (fewer than 512
- * blocks of 128 keys over all KV heads), fp32 partial dK and dV per row
- * chunk; deterministic in the sizes. That much is required. For bf16 the
+ * fp32 D and LSE values and, for bf16 on short sequences (one KV head: fewer
+ * than 512 blocks of 128 keys, up to 16 row chunks; several KV heads: fewer
+ * than 1024 (block, KV head) pairs, 2 row chunks), fp32 partial dK and dV per
+ * row chunk; deterministic in the sizes. That much is required. For bf16 the
  * size returned also holds room for up to 8 key splits of dQ when the dQ grid
  * has fewer than 1024 workgroups (fp32 partial dQ of every row, summed in a
  * fixed order afterwards; see usp_attn_bwd_num_splits): about 134 MB at

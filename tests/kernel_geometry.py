@@ -266,10 +266,16 @@ def kmajor(s_pad, heads, d, s_t, t: Touch):
 def dkdv_row_chunks(s_q, s_k, hkv):
     keys = 128
     items = -(-s_k // keys) * hkv
-    if items >= 512:
-        return 1
     tiles = -(-s_q // 64)
-    n = min(-(-2048 // items), tiles, 16)
+    if hkv == 1:
+        if items >= 512:
+            return 1
+        n = min(-(-4096 // items), 16)
+    else:
+        if items >= 1024:
+            return 1
+        n = 2
+    n = min(n, tiles)
     return n if n > 1 else 1
 
 

@@ -229,13 +229,20 @@ def test_merge_argument_errors(L):
 
 
 def dkdv_chunks(s_q, s_k, hkv):
-    """Row chunks per key block of the bf16 dK/dV kernel: 1 when the 128-key
-    blocks give at least 512 workgroups, else enough for about 2048 (block,
-    chunk) items, at most 16 and at most the number of 64-row tiles."""
+    """Row chunks per key block of the bf16 dK/dV kernel. One KV head: 1 when
+    the 128-key blocks number at least 512, else enough for about 4096 (block,
+    chunk) items, at most 16. Several KV heads: 1 from 1024 (block, head)
+    items, else 2. Never more than the number of 64-row tiles."""
     items = -(-s_k // 128) * hkv
-    if items >= 512:
-        return 1
-    return max(1, min(-(-2048 // items), -(-s_q // 64), 16))
+    if hkv == 1:
+        if items >= 512:
+            return 1
+        n = min(-(-4096 // items), 16)
+    else:
+        if items >= 1024:
+            return 1
+        n = 2
+    return max(1, min(n, -(-s_q // 64)))
 
 
 def dq_split_cap(s_q, hq, hkv):
@@ -264,7 +271,8 @@ def test_workspace_sizes(L):
         # D and LSE * log2(e) per (head, row), fp32
         assert 2 * 4 * s * 4 <= b - part < 2 * 4 * (s + 128) * 4 + 512
     assert dkdv_chunks(120000, 120000, 1) == 1 and dkdv_chunks(8192, 8192, 1) == 16
-    assert dkdv_chunks(32768, 32768, 1) == 8 and dkdv_chunks(100, 100, 1) == 2
+    assert dkdv_chunks(32768, 32768, 1) == 16 and dkdv_chunks(100, 100, 1) == 2
+    assert dkdv_chunks(8192, 8192, 8) == 2 and dkdv_chunks(8192, 8192, 16) == 1
     assert L.usp_attn_fwd_workspace_bytes(512, 4, 2, 64, FP32) == 0
     assert L.usp_attn_bwd_workspace_bytes(512, 4, 2, 64, FP32) == 512 * 4 * 4
     assert L.usp_attn_fwd_workspace_bytes(0, 4, 1, 128, BF16) == 0

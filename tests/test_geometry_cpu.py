@@ -99,8 +99,8 @@ def full_cases():
     for c in SMALL:
         name, s, s_valid, hq, hkv, cu, causal = c[:7]
         out.append((name, s, s_valid, hq, hkv, cu, causal, c[7] if len(c) > 7 else 128))
-    for name, s, s_valid, cu, causal, d in LONG:
-        out.append((name, s, s_valid, 32, 8, cu, causal, d))
+    for name, s, s_valid, cu, causal, d, hq, hkv in LONG:
+        out.append((name, s, s_valid, hq, hkv, cu, causal, d))
     out += [tuple(c) for c in FULL]
     for name, w in workloads.WORKLOADS.items():
         if w.dtype != "bf16":

@@ -230,16 +230,19 @@ def oracle_by_group(q64, k64, v64, do64, scale, s_valid, cu, causal):
     return cat
 
 
-# Every kernel on its long-sequence path: 32 Q / 8 KV heads (the 8K workload's
-# full model on one GPU), d = 128, 8192 tokens. The dK/dV grid then has 512
-# blocks of 128 keys (one row chunk: the direct-store epilogue of the 120K
-# step), the forward 1024 workgroups and dQ 2048 (one pass each, no key
-# splits), so no reduction or merge kernel runs. Compared element by element.
+# Every kernel on its long-sequence path: 64 Q / 16 KV heads at 8192 tokens,
+# d = 128. The dK/dV grid then has 1024 (block of 128 keys, KV head) items,
+# one row chunk each (the direct-store epilogue of the 120K step), the forward
+# 2048 workgroups and dQ 4096 (one pass each, no key splits), so no
+# reduction or merge kernel runs. The 8K workload's full model (32 Q / 8 KV)
+# runs its dK/dV in two row chunks plus the reduction. Compared element by
+# element.
 LONG = [
-    # name, S, s_valid, cu_seqlens, causal, d
-    ("long_8k_32q8kv", 8192, 8192, None, True, 128),
-    ("long_8k_32q8kv_padded", 8192, 8190, None, True, 128),
-    ("long_8k_32q8kv_docs", 8192, 8192, [0, 1000, 1001, 5000, 8192], True, 128),
+    # name, S, s_valid, cu_seqlens, causal, d, hq, hkv
+    ("long_8k_64q16kv", 8192, 8192, None, True, 128, 64, 16),
+    ("long_8k_64q16kv_padded", 8192, 8190, None, True, 128, 64, 16),
+    ("long_8k_64q16kv_docs", 8192, 8192, [0, 1000, 1001, 5000, 8192], True, 128, 64, 16),
+    ("long_8k_32q8kv_two_chunks", 8192, 8192, None, True, 128, 32, 8),
 ]
 SINGLE_PASS = {"attn_fwd_kmajor_v", "attn_fwd_bf16", "attn_bwd_rowdot_bf16",
                "attn_bwd_dkdv_bf16", "attn_bwd_dq_bf16"}
@@ -247,8 +250,7 @@ SINGLE_PASS = {"attn_fwd_kmajor_v", "attn_fwd_bf16", "attn_bwd_rowdot_bf16",
 
 @pytest.mark.parametrize("case", LONG, ids=[c[0] for c in LONG])
 def test_bf16_long_path_full_compare(case):
-    name, s, s_valid, cu, causal, d = case
-    hq, hkv = 32, 8
+    name, s, s_valid, cu, causal, d, hq, hkv = case
     L = usp()
     dev = gpu()
     say(f"bf16 {name}: S={s} s_valid={s_valid} hq={hq} hkv={hkv} d={d}")
@@ -266,7 +268,8 @@ def test_bf16_long_path_full_compare(case):
         ran = {e["name"] for e in L.usp_trace_collect()}
     finally:
         L.usp_trace_enable(False)
-    assert ran == SINGLE_PASS, ran
+    want = SINGLE_PASS | ({"attn_bwd_dkdv_reduce"} if hkv == 8 else set())
+    assert ran == want, ran
     say(f"  oracle, {hkv} groups in parallel")
     o, lse, dq, dk, dv = oracle_by_group(*(f64(t) for t in (q, k, v, do)), d ** -0.5, s_valid, cu,
                                           causal)

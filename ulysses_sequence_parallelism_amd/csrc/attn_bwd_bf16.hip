@@ -810,20 +810,32 @@ constexpr int kDkdvRows = 64;    // query rows per dK/dV tile
 constexpr int kDkdvGroups = 4;   // 32-key groups (wave pairs) per dK/dV workgroup
 
 // Row chunks per key block in the dK/dV kernel. When the key blocks alone give
-// fewer than 512 workgroups (short sequences: 64 at 8K tokens on one KV head)
-// most compute units would sit idle, and under a causal mask the first blocks
-// walk many times the rows of the last, so each key block's rows are split to
-// give about 2048 (key block, chunk) items, at most 16 chunks per block (at 8K
-// on one KV head, 32 chunks were slower than 16; at 16K and 32K, 16 and 8
-// chunks were 11% and 16% faster than 8 and 4).
+// too few workgroups, most compute units would sit idle, and under a causal
+// mask the first blocks walk many times the rows of the last, so each key
+// block's rows are split into chunks whose fp32 partials a reduction adds. The
+// counts come from a sweep of 1..32 chunks (dK/dV kernel plus reduction,
+// d = 128): on one KV head the best counts give about 4096 (key block, chunk)
+// items, at most 16 chunks (4K: 84 us at 16 chunks, 72 at 8; 8K: 201 at 16;
+// 16K: 603 at 16; 32K: 2137 at 16, 2266 at 8), and from 512 blocks one pass
+// (120K: 2 chunks tie with 1). With several KV heads the partials' traffic
+// grows with the head count and 2 chunks are best below 1024 items (4100
+// tokens, 16 Q / 4 KV: 231 us against 286 at 16; 8K, 32 Q / 8 KV: 1287
+// against 1663 in one pass). A dispatch simulation of the kind that plans the
+// key splits ranked these counts poorly (it picked 6 at 8K and 2 at 32K).
 int dkdv_row_chunks(int64_t s_q, int64_t s_k, int hkv) {
   constexpr int keys = 32 * kDkdvGroups;
   const int64_t items = (s_k + keys - 1) / keys * hkv;
-  if (items >= 512) return 1;
   const int64_t tiles = (s_q + kDkdvRows - 1) / kDkdvRows;
-  int64_t n = (2048 + items - 1) / items;
+  int64_t n;
+  if (hkv == 1) {
+    if (items >= 512) return 1;
+    n = (4096 + items - 1) / items;
+    n = n < 16 ? n : 16;
+  } else {
+    if (items >= 1024) return 1;
+    n = 2;
+  }
   n = n < tiles ? n : tiles;
-  n = n < 16 ? n : 16;
   return n > 1 ? (int)n : 1;
 }
 
