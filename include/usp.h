@@ -98,7 +98,14 @@ int usp_unpack_head2seq(const void* y, void* x, int64_t s_real, int p, int h, in
  * usp_attn_fwd_num_splits). The room is for min(8, ceil(1024 / workgroups))
  * splits: about 135 MB at s_pad = 8192 with 4 query heads, one KV head and
  * d = 128 (8 splits) or at 16,384 (4 splits); none from 32,768 rows per KV
- * head at 4:1 GQA upwards.
+ * head at 4:1 GQA upwards. Without splits the room holds a small table
+ * instead (12 bytes per block of query rows, 256-byte aligned): a call with
+ * cu_seqlens runs its query blocks longest first, an order two small kernels
+ * compute from the documents (within one document the work of a block grows
+ * with its position; the natural order, last block first, is longest first
+ * only for a single sequence). The order only schedules the same per-block
+ * arithmetic: outputs are bit for bit those of the natural order, which a
+ * call without room for the table keeps.
  */
 size_t usp_attn_fwd_workspace_bytes(int64_t s_pad, int hq, int hkv, int d, int dtype);
 
@@ -143,8 +150,12 @@ int usp_attn_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  * has fewer than 1024 workgroups (fp32 partial dQ of every row, summed in a
  * fixed order afterwards; see usp_attn_bwd_num_splits): about 134 MB at
  * s_pad = 8192 with 4 query heads and d = 128. With less room the call splits
- * less (one pass with none), same results up to rounding. The whole
- * workspace_bytes range must not overlap the other arguments. */
+ * less (one pass with none), same results up to rounding. Without splits or
+ * row chunks the room holds two small tables instead (12 bytes per block of
+ * 128 keys and per dQ block of query rows), with which a call with
+ * cu_seqlens runs both kernels' blocks longest first, as usp_attn_fwd does
+ * (same outputs bit for bit). The whole workspace_bytes range must not
+ * overlap the other arguments. */
 size_t usp_attn_bwd_workspace_bytes(int64_t s_pad, int hq, int hkv, int d, int dtype);
 
 /*

@@ -504,3 +504,33 @@ def merge(s_q, hq, d, t: Touch):
         t.add(b, e, e + 3)
     for b in ("lse_a", "lse_b", "lse"):
         t.add(b, li, li)
+
+
+# ---------------------------------------------------------------------------
+# longest-first block order of calls with documents (splits.hip)
+
+def block_costs(m: Geom, kind, n, block, tile):
+    """Tiles each block walks: kind 0, query blocks of `block` rows over key
+    tiles of `tile`; kind 1, key blocks of `block` keys over row tiles of
+    `tile` (as block_cost_kernel)."""
+    b = np.arange(n, dtype=I64)
+    if kind == 0:
+        q0 = b * block
+        q1 = np.minimum(q0 + block, m.s_q)
+        lo, _ = m.row_keys(q0)
+        _, hi = m.row_keys(q1 - 1)
+        t0 = cdiv(lo, tile) * tile
+        return np.where(hi >= lo, cdiv(hi - t0, tile) + 1, 0)
+    j0 = b * block
+    j1 = np.minimum(j0 + block, m.s_k)
+    rf_lo, _ = m.key_rows(j0)
+    _, rl_hi = m.key_rows(j1 - 1)
+    rstart = np.maximum(rf_lo, 0)
+    rend = rl_hi - 1
+    return np.where((j0 < m.s_kv) & (rend >= rstart), cdiv(rend, tile) - cdiv(rstart, tile) + 1, 0)
+
+
+def longest_first(cost):
+    """Block indexes by decreasing cost, ties by index."""
+    cost = np.asarray(cost)
+    return np.lexsort((np.arange(len(cost)), -cost))

@@ -255,9 +255,23 @@ def dq_split_cap(s_q, hq, hkv):
     return 1 if wgs >= 1024 else min(8, -(-2048 // wgs))
 
 
-def dq_room(s_q, hq, hkv, d):
+def order_bytes(n):
+    """A block order table of n blocks: costs, ranks, then the order (int32
+    each, 256-byte aligned)."""
+    return 3 * (-(-n * 4 // 256) * 256)
+
+
+def dq_room(s_q, hq, hkv, d, s_k=None):
+    """Room the backward workspace query adds beyond the required part: the dQ
+    key-split partials, or the two block orders of a call with documents (dK/dV
+    key blocks of 128, dQ query blocks of 32 (4 / HG) rows), whichever is
+    larger (the two are never used together)."""
+    s_k = s_q if s_k is None else s_k
     z = dq_split_cap(s_q, hq, hkv)
-    return z * s_q * hq * d * 4 if z > 1 else 0
+    g = hq // hkv
+    hg = 4 if g % 4 == 0 else 2 if g % 2 == 0 else 1
+    orders = order_bytes(-(-s_k // 128)) + order_bytes(-(-s_q // (32 * (4 // hg))))
+    return max(z * s_q * hq * d * 4 if z > 1 else 0, orders)
 
 
 def test_workspace_sizes(L):
@@ -280,7 +294,7 @@ def test_workspace_sizes(L):
     for s_q, s_k in ((100, 1000), (1000, 100), (512, 512), (30000, 30000)):
         for hkv, d in ((1, 128), (4, 64)):
             b = L.usp_attn_bwd_interval_workspace_bytes(s_q, s_k, 4 * hkv, hkv, d, BF16)
-            b -= dq_room(s_q, 4 * hkv, hkv, d)
+            b -= dq_room(s_q, 4 * hkv, hkv, d, s_k)
             n = dkdv_chunks(s_q, s_k, hkv)
             part = 2 * n * s_k * hkv * d * 4 if n > 1 else 0
             assert 2 * 4 * hkv * s_q * 4 <= b - part < 2 * 4 * hkv * (s_q + 128) * 4 + 512
@@ -305,8 +319,13 @@ def test_fwd_workspace_and_key_splits(L):
                           (32768, 4, 1, 128), (1000, 8, 2, 64), (120000, 4, 1, 128),
                           (131072, 16, 4, 128), (64, 4, 1, 128)):
         z = fwd_split_cap(s, hq, hkv)
-        # fp32 partial O (256-byte aligned) and LSE per split
+        # fp32 partial O (256-byte aligned) and LSE per split, or the block
+        # order of a call with documents (query blocks of 32 (8 / HG) rows),
+        # whichever is larger
         room = (-(-z * s * hq * d * 4 // 256) * 256 + z * hq * s * 4) if z > 1 else 0
+        g = hq // hkv
+        hg = 4 if g % 4 == 0 else 2 if g % 2 == 0 else 1
+        room = max(room, order_bytes(-(-s // (32 * (8 // hg)))))
         ws = L.usp_attn_fwd_workspace_bytes(s, hq, hkv, d, BF16)
         assert ws == vcopy(s, hkv, d) + room
         for causal in (0, 1):

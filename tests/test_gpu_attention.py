@@ -268,7 +268,9 @@ def test_bf16_long_path_full_compare(case):
         ran = {e["name"] for e in L.usp_trace_collect()}
     finally:
         L.usp_trace_enable(False)
-    want = SINGLE_PASS | ({"attn_bwd_dkdv_reduce"} if hkv == 8 else set())
+    # with documents the blocks also run longest first (a plan kernel pair)
+    want = SINGLE_PASS | ({"attn_bwd_dkdv_reduce"} if hkv == 8 else set()) | \
+        ({"attn_block_order"} if cu is not None else set())
     assert ran == want, ran
     say(f"  oracle, {hkv} groups in parallel")
     o, lse, dq, dk, dv = oracle_by_group(*(f64(t) for t in (q, k, v, do)), d ** -0.5, s_valid, cu,
@@ -278,6 +280,56 @@ def test_bf16_long_path_full_compare(case):
     check_close("dQ", f64(got["dq"]), dq, "bf16")
     check_close("dK", f64(got["dk"]), dk, "bf16")
     check_close("dV", f64(got["dv"]), dv, "bf16")
+
+
+def test_bf16_document_block_order_only_schedules():
+    """With packed documents and one pass per kernel, the forward, dK/dV and dQ
+    run their blocks longest first (an order computed on the device from the
+    documents). The order only schedules: the outputs equal, bit for bit,
+    those of calls whose workspace has no room for it (natural order)."""
+    L = usp()
+    dev = gpu()
+    s, hq, hkv, d = 8192, 64, 16, 128
+    cu = [0, 1000, 1001, 5000, 8192]
+    say(f"block order: S={s} hq={hq} hkv={hkv} docs={cu}")
+    q, k, v, do = (seeded((s, h, d), 5200 + i, torch.bfloat16).to(dev)
+                   for i, h in enumerate((hq, hkv, hkv, hq)))
+    fw_min = torch.empty(hkv * d * ((s + 127) // 128 * 128) * 2, dtype=torch.uint8, device=dev)
+    L.usp_trace_collect()
+    L.usp_trace_enable(True)
+    try:
+        o1, l1 = L.usp_attn_fwd(q, k, v, cu_seqlens=cu)
+        g1 = L.usp_attn_bwd(q, k, v, o1, l1, do, cu_seqlens=cu)
+        torch.cuda.synchronize()
+        ran = {e["name"]: e["launches"] for e in L.usp_trace_collect()}
+        o2, l2 = L.usp_attn_fwd(q, k, v, cu_seqlens=cu, workspace=fw_min)
+        need = L.usp_attn_bwd_workspace_bytes(s, hq, hkv, d, L.USP_BF16)
+        bw_min = torch.empty(need - 1, dtype=torch.uint8, device=dev)  # no room for the orders
+        g2 = L.usp_attn_bwd(q, k, v, o1, l1, do, cu_seqlens=cu, workspace=bw_min)
+        torch.cuda.synchronize()
+        ran2 = {e["name"] for e in L.usp_trace_collect()}
+    finally:
+        L.usp_trace_enable(False)
+    assert ran.get("attn_block_order") == 3, ran  # forward, dK/dV, dQ
+    assert "attn_block_order" not in ran2, ran2
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    # the forward's order, read back from its workspace (after the V copy:
+    # costs, ranks, then the order), against the CPU replica of the costs
+    from tests import kernel_geometry as G
+    fw = torch.empty(L.usp_attn_fwd_workspace_bytes(s, hq, hkv, d, L.USP_BF16), dtype=torch.uint8,
+                     device=dev)
+    L.usp_attn_fwd(q, k, v, cu_seqlens=cu, workspace=fw)
+    torch.cuda.synchronize()
+    n = -(-s // 64)                            # query blocks of 64 rows (4 heads x 2 x 32)
+    part = -(-n * 4 // 256) * 256
+    base = hkv * d * ((s + 127) // 128 * 128) * 2
+    tab = fw[base:base + 3 * part].cpu().view(torch.int32).numpy()
+    m = G.Geom(s_q=s, s_k=s, s_kv=s, cu=cu)
+    cost = G.block_costs(m, 0, n, 64, 64)
+    np.testing.assert_array_equal(tab[:n], cost)
+    np.testing.assert_array_equal(tab[2 * part // 4:2 * part // 4 + n], G.longest_first(cost))
 
 
 def key_fixture(name):

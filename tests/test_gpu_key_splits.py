@@ -37,7 +37,7 @@ def vcopy_bytes(s_k, hkv, d):
 def bwd_workspaces(L, s_q, s_k, hq, hkv, d, dev):
     """(workspace the query returns, its required part alone) for the backward."""
     full = L.usp_attn_bwd_interval_workspace_bytes(s_q, s_k, hq, hkv, d, L.USP_BF16)
-    req = full - dq_room(s_q, hq, hkv, d)
+    req = full - dq_room(s_q, hq, hkv, d, s_k)
     return (torch.empty(full, dtype=torch.uint8, device=dev),
             torch.empty(req, dtype=torch.uint8, device=dev))
 

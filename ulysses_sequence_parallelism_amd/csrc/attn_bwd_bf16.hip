@@ -112,6 +112,10 @@ struct BwdParams {
   int64_t dq_stride;
   int grad_f32, accum;  // fp32 gradients; add to the existing contents
   float scale, scale_log2;
+  // longest-first order of the dK/dV key blocks and of the dQ query blocks
+  // (calls with packed documents, one pass each), or NULL: the natural order
+  const int* kv_order;
+  const int* q_order;
 };
 
 // Write DB x 4 accumulator values (registers 4r..4r+3 of block b go to
@@ -198,7 +202,9 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
   const int kvh = blockIdx.y;
   // (key block, row chunk) of this workgroup, chunk-major: the workgroups
   // resident together work on the same rows
-  const int cch = (int)blockIdx.x / pr.n_kb, kbi = (int)blockIdx.x % pr.n_kb;
+  const int cch = (int)blockIdx.x / pr.n_kb;
+  const int kbi = pr.kv_order ? order_entry(pr.kv_order, (int)blockIdx.x % pr.n_kb)
+                              : (int)blockIdx.x % pr.n_kb;
   const int j0 = kbi * KEYS;
   const int j1 = min(j0 + KEYS, s_k);
   const int wj0 = j0 + grp * 32;
@@ -563,7 +569,8 @@ __global__ __launch_bounds__(256, (BN == 32 ? 2 : 1)) void bwd_dq_kernel(BwdPara
   const int head = kvh * g + hc * HG + (w % HG);
   // heaviest query block first; its key splits follow one another, the
   // order rotated by the block when their count is even (see the forward)
-  const int qb = pr.n_blocks - 1 - (int)blockIdx.x / pr.dq_split;
+  const int bi = (int)blockIdx.x / pr.dq_split;
+  const int qb = pr.q_order ? order_entry(pr.q_order, bi) : pr.n_blocks - 1 - bi;
   const int zk = (int)blockIdx.x % pr.dq_split;
   const int zs = (pr.dq_split & 1) ? zk : (zk + qb) % pr.dq_split;
   const int q0 = qb * QROWS;
@@ -958,6 +965,14 @@ size_t bwd_required(int64_t s_q, int64_t s_k, int hq, int hkv, int d) {
   return rows + align256(n_ch > 1 ? (size_t)2 * n_ch * (size_t)s_k * hkv * d * 4 : 0);
 }
 
+// Bytes of the two block orders: key blocks of the dK/dV kernel, then query
+// blocks of the dQ kernel.
+size_t bwd_order_bytes(int64_t s_q, int64_t s_k, int hq, int hkv) {
+  constexpr int keys = 32 * kDkdvGroups;
+  return block_order_bytes((s_k + keys - 1) / keys) +
+         block_order_bytes((s_q + dq_qrows(hq, hkv) - 1) / dq_qrows(hq, hkv));
+}
+
 SplitPlan plan_dq_for(const AttnArgs& a) {
   const size_t req = bwd_required(a.s_q, a.s_k, a.hq, a.hkv, a.d);
   const size_t room = a.workspace_bytes > req ? a.workspace_bytes - req : 0;
@@ -966,9 +981,13 @@ SplitPlan plan_dq_for(const AttnArgs& a) {
 
 }  // namespace
 
-// The required part, then room for the dQ key splits of s_q rows.
+// The required part, then room for the dQ key splits of s_q rows, or for the
+// block orders of the dK/dV key blocks and the dQ query blocks (used only
+// without splits or row chunks).
 size_t attn_bwd_bf16_workspace(int64_t s_q, int64_t s_k, int hq, int hkv, int d) {
-  return bwd_required(s_q, s_k, hq, hkv, d) + dq_split_bytes(dq_split_cap(s_q, hq, hkv), s_q, hq, d);
+  return bwd_required(s_q, s_k, hq, hkv, d) +
+         std::max(dq_split_bytes(dq_split_cap(s_q, hq, hkv), s_q, hq, d),
+                  bwd_order_bytes(s_q, s_k, hq, hkv));
 }
 
 size_t attn_bwd_bf16_min_workspace(int64_t s_q, int64_t s_k, int hq, int hkv, int d) {
@@ -1003,10 +1022,26 @@ int attn_bwd_bf16(const AttnArgs& a) {
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
   const SplitPlan dp = plan_dq_for(a);
+  const size_t req = bwd_required(a.s_q, a.s_k, a.hq, a.hkv, a.d);
   p.dq_split = dp.n_split;
   p.dq_tiles = dp.split_tiles;
-  p.dq_part = reinterpret_cast<float*>(ws + bwd_required(a.s_q, a.s_k, a.hq, a.hkv, a.d));
+  p.dq_part = reinterpret_cast<float*>(ws + req);
   p.dq_stride = a.s_q * a.hq * a.d;
+  // packed documents, one pass in both kernels: their blocks longest first,
+  // planned in the room the dQ splits would use
+  const size_t room = a.workspace_bytes > req ? a.workspace_bytes - req : 0;
+  if (a.cu != nullptr && dp.n_split <= 1 && dkdv_row_chunks(a.s_q, a.s_k, a.hkv) == 1 &&
+      room >= bwd_order_bytes(a.s_q, a.s_k, a.hq, a.hkv)) {
+    constexpr int keys = 32 * kDkdvGroups;
+    const int n_kb = (int)((a.s_k + keys - 1) / keys);
+    const int qrows = dq_qrows(a.hq, a.hkv);
+    int rc = block_order_launch(p.m, kOrderKeyBlocks, n_kb, keys, kDkdvRows, ws + req, a.stream,
+                                &p.kv_order);
+    if (rc != USP_OK) return rc;
+    rc = block_order_launch(p.m, kOrderQueryBlocks, (int)((a.s_q + qrows - 1) / qrows), qrows,
+                            kDqKeys, ws + req + block_order_bytes(n_kb), a.stream, &p.q_order);
+    if (rc != USP_OK) return rc;
+  }
   return a.d == 64 ? bwd_launch<64>(p, a, dd, lse2, part) : bwd_launch<128>(p, a, dd, lse2, part);
 }
 

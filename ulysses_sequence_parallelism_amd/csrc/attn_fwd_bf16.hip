@@ -86,6 +86,9 @@ struct FwdParams {
   // fp32 partial O / LSE at o32 + z * o_split and lse + z * lse_split.
   int n_split, split_tiles;
   int64_t o_split, lse_split;
+  // longest-first order of the query blocks (calls with packed documents), or
+  // NULL: the natural order, last block first
+  const int* order;
 };
 
 template <int D, int HG>
@@ -117,7 +120,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
   // even count the order is rotated by the block, so that the round-robin
   // over the 8 dies does not send every block's first piece to the same dies
   // (an odd count is coprime with 8 and keeps the full pieces first).
-  const int qb = pr.n_qblocks - 1 - (int)blockIdx.x / pr.n_split;
+  const int bi = (int)blockIdx.x / pr.n_split;
+  const int qb = pr.order ? order_entry(pr.order, bi) : pr.n_qblocks - 1 - bi;
   const int zk = (int)blockIdx.x % pr.n_split;
   const int zs = (pr.n_split & 1) ? zk : (zk + qb) % pr.n_split;
   const int q0 = qb * QROWS;
@@ -526,9 +530,16 @@ int split_merge_launch(const float* part, const float* plse, int64_t o_split, in
 
 }  // namespace
 
-// The V copy, then room for the key splits of a call of s_k query rows.
+// Bytes of the longest-first block order of s_q query rows.
+static size_t fwd_order_bytes(int64_t s_q, int hq, int hkv) {
+  return block_order_bytes((s_q + qrows_for(hq, hkv) - 1) / qrows_for(hq, hkv));
+}
+
+// The V copy, then room for the key splits of a call of s_k query rows, or for
+// its block order (used only without splits).
 size_t attn_fwd_bf16_workspace(int64_t s_k, int hq, int hkv, int d) {
-  return vcopy_bytes(s_k, hkv, d) + split_bytes(split_cap(s_k, hq, hkv), s_k, hq, d);
+  return vcopy_bytes(s_k, hkv, d) +
+         std::max(split_bytes(split_cap(s_k, hq, hkv), s_k, hq, d), fwd_order_bytes(s_k, hq, hkv));
 }
 
 size_t attn_fwd_bf16_min_workspace(int64_t s_k, int hkv, int d) { return vcopy_bytes(s_k, hkv, d); }
@@ -572,6 +583,14 @@ int attn_fwd_bf16(const AttnArgs& a) {
   } else {
     p.o = a.out_f32 ? nullptr : static_cast<__bf16*>(a.o_out);
     p.o32 = a.out_f32 ? static_cast<float*>(a.o_out) : nullptr;
+  }
+  // packed documents, one pass: the query blocks longest first, planned in
+  // the room the splits would use
+  if (a.cu != nullptr && sp.n_split <= 1 && room >= fwd_order_bytes(a.s_q, a.hq, a.hkv)) {
+    const int qrows = qrows_for(a.hq, a.hkv);
+    rc = block_order_launch(p.m, kOrderQueryBlocks, (int)((a.s_q + qrows - 1) / qrows), qrows, BN,
+                            static_cast<char*>(a.workspace) + v, a.stream, &p.order);
+    if (rc != USP_OK) return rc;
   }
   const int g = a.hq / a.hkv;
   rc = a.d == 64 ? fwd_dispatch<64>(p, g, a.hkv, a.stream) : fwd_dispatch<128>(p, g, a.hkv, a.stream);

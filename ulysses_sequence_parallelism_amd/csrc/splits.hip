@@ -12,6 +12,7 @@
 #include <queue>
 #include <vector>
 
+#include "usp_common.h"
 #include "usp_internal.h"
 
 namespace usp {
@@ -73,6 +74,102 @@ SplitPlan plan_key_splits(const SplitProblem& p) {
     }
   }
   return best;
+}
+
+// ---------------------------------------------------------------------------
+// Longest-first block order for calls with packed documents. Without
+// documents the grids already run their blocks longest-first (the causal
+// triangle's work grows with the query block and shrinks with the key block);
+// with documents every document is its own triangle, so that order
+// interleaves long and short blocks. These two kernels give a permutation of
+// the blocks by decreasing work, ties by block index (the plan is
+// deterministic); the attention kernels then map workgroup b to block
+// order[b]. The order only schedules: every block's arithmetic is unchanged.
+
+namespace {
+
+// Work of each block in tiles: query blocks of `block` rows walk the key tiles
+// of `tile` keys from the tile of their first row's first key to their last
+// row's last key (the forward and dQ tile ranges); key blocks of `block` keys
+// walk the row tiles of `tile` rows from their first key's first row to their
+// last key's last row (the dK/dV range), none past the valid keys. Also
+// clears the rank counts.
+__global__ __launch_bounds__(256) void block_cost_kernel(MaskGeom m, int kind, int n, int block,
+                                                         int tile, int* __restrict__ cost,
+                                                         int* __restrict__ rank) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= n) return;
+  int c = 0;
+  if (kind == kOrderQueryBlocks) {
+    const int q0 = b * block, q1 = min(q0 + block, m.s_q);
+    const KeyRange kf = row_keys(m, q0), kl = row_keys(m, q1 - 1);
+    const int t0 = kf.lo / tile * tile;
+    c = kl.hi >= kf.lo ? (kl.hi - t0) / tile + 1 : 0;
+  } else {
+    const int j0 = b * block, j1 = min(j0 + block, m.s_k);
+    const RowSpan rf = key_rows(m, j0), rl = key_rows(m, j1 - 1);
+    const int rstart = max(rf.lo, 0), rend = rl.hi - 1;
+    c = (j0 < m.s_kv && rend >= rstart) ? rend / tile - rstart / tile + 1 : 0;
+  }
+  cost[b] = c;
+  rank[b] = 0;
+}
+
+// rank(i) = #{j : cost_j > cost_i} + #{j < i : cost_j = cost_i}, counted over
+// j in chunks of 256 (grid y) held in LDS and read 4 at a time; the chunk
+// counts are added with integer atomics (a sum: the result does not depend on
+// their order).
+__global__ __launch_bounds__(256) void block_rank_kernel(const int* __restrict__ cost, int n,
+                                                         int* __restrict__ rank) {
+  __shared__ __attribute__((aligned(16))) int chunk[256];
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int j0 = blockIdx.y * 256;
+  // past the end: a cost no block has (-1), never counted
+  chunk[threadIdx.x] = j0 + (int)threadIdx.x < n ? cost[j0 + threadIdx.x] : -1;
+  __syncthreads();
+  if (i >= n) return;
+  const int ci = cost[i];
+  const int rel = i - j0;  // chunk positions below rel precede i
+  int r = 0;
+#pragma unroll 8
+  for (int t = 0; t < 256; t += 4) {
+    const int4 c4 = *reinterpret_cast<const int4*>(&chunk[t]);
+    r += (c4.x > ci || (c4.x == ci && t < rel)) ? 1 : 0;
+    r += (c4.y > ci || (c4.y == ci && t + 1 < rel)) ? 1 : 0;
+    r += (c4.z > ci || (c4.z == ci && t + 2 < rel)) ? 1 : 0;
+    r += (c4.w > ci || (c4.w == ci && t + 3 < rel)) ? 1 : 0;
+  }
+  if (r != 0) atomicAdd(&rank[i], r);
+}
+
+// order[rank(i)] = i: the ranks are a permutation of [0, n).
+__global__ __launch_bounds__(256) void block_scatter_kernel(const int* __restrict__ rank, int n,
+                                                            int* __restrict__ order) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) order[rank[i]] = i;
+}
+
+}  // namespace
+
+size_t block_order_bytes(int64_t n) { return (size_t)((n * 4 + 255) / 256 * 256) * 3; }
+
+int block_order_launch(const MaskGeom& m, int kind, int n, int block, int tile, void* room,
+                       hipStream_t stream, const int** order) {
+  const size_t part = block_order_bytes(n) / 3;
+  int* cost = static_cast<int*>(room);
+  int* rank = reinterpret_cast<int*>(static_cast<char*>(room) + part);
+  int* ord = reinterpret_cast<int*>(static_cast<char*>(room) + 2 * part);
+  const unsigned nb = (unsigned)((n + 255) / 256);
+  TraceScope ts("attn_block_order", stream);
+  hipLaunchKernelGGL(block_cost_kernel, dim3(nb), dim3(256), 0, stream, m, kind, n, block, tile,
+                     cost, rank);
+  if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
+  hipLaunchKernelGGL(block_rank_kernel, dim3(nb, nb), dim3(256), 0, stream, cost, n, rank);
+  if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
+  hipLaunchKernelGGL(block_scatter_kernel, dim3(nb), dim3(256), 0, stream, rank, n, ord);
+  if (hipGetLastError() != hipSuccess) return USP_ERR_HIP;
+  *order = ord;
+  return USP_OK;
 }
 
 }  // namespace usp

@@ -224,6 +224,14 @@ __device__ __forceinline__ RowSpan key_rows(const MaskGeom& m, int c) {
   return {max(b.lo, m.causal ? gj : 0) - m.q_off, min(b.hi - m.q_off, m.s_q)};
 }
 
+// Entry b of a block order table (see block_order_launch), read through the
+// scalar cache: the table is not written while a kernel that reads it runs,
+// and b is wave-uniform.
+__device__ __forceinline__ int order_entry(const int* order, int b) {
+  typedef __attribute__((address_space(4))) const int* ConstInt;
+  return ((ConstInt)(uintptr_t)order)[__builtin_amdgcn_readfirstlane(b)];
+}
+
 // Key-major workspace row length: padded so every 64-key tile is in bounds.
 __host__ __device__ __forceinline__ int64_t kmajor_len(int64_t s_pad) {
   return (s_pad + 127) / 128 * 128;

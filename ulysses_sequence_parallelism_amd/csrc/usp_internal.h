@@ -124,6 +124,16 @@ struct SplitPlan {
 };
 SplitPlan plan_key_splits(const SplitProblem& p);
 
+// Longest-first order of a grid's blocks for calls with packed documents
+// (splits.hip): kind kOrderQueryBlocks (blocks of `block` query rows over key
+// tiles of `tile`) or kOrderKeyBlocks (blocks of `block` keys over row tiles of
+// `tile`). Needs block_order_bytes(n) bytes of device memory at `room`; on
+// success *order points into it (n block indexes, longest first).
+enum { kOrderQueryBlocks = 0, kOrderKeyBlocks = 1 };
+size_t block_order_bytes(int64_t n);
+int block_order_launch(const MaskGeom& m, int kind, int n, int block, int tile, void* room,
+                       hipStream_t stream, const int** order);
+
 size_t attn_fwd_bf16_workspace(int64_t s_k, int hq, int hkv, int d);
 size_t attn_fwd_bf16_min_workspace(int64_t s_k, int hkv, int d);  // the V copy alone
 size_t attn_bwd_bf16_workspace(int64_t s_q, int64_t s_k, int hq, int hkv, int d);
