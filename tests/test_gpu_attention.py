@@ -315,6 +315,30 @@ def test_bf16_document_block_order_only_schedules():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+    # a contiguous context-parallel rank's rows (global offset, global
+    # documents) against every key: also ordered, also bit-identical
+    qa = s // 2
+    L.usp_trace_collect()
+    L.usp_trace_enable(True)
+    try:
+        o3, l3 = L.usp_attn_fwd_interval(q[qa:], k, v, q_off=qa, cu_seqlens=cu,
+                                         out_dtype=torch.bfloat16)
+        g3 = L.usp_attn_bwd_interval(q[qa:], k, v, o3, l3, do[qa:], q_off=qa, cu_seqlens=cu)
+        torch.cuda.synchronize()
+        ran3 = {e["name"]: e["launches"] for e in L.usp_trace_collect()}
+        o4, l4 = L.usp_attn_fwd_interval(q[qa:], k, v, q_off=qa, cu_seqlens=cu,
+                                         out_dtype=torch.bfloat16, workspace=fw_min)
+        nb = L.usp_attn_bwd_interval_workspace_bytes(s - qa, s, hq, hkv, d, L.USP_BF16)
+        g4 = L.usp_attn_bwd_interval(q[qa:], k, v, o3, l3, do[qa:], q_off=qa, cu_seqlens=cu,
+                                     workspace=torch.empty(nb - 1, dtype=torch.uint8, device=dev))
+        torch.cuda.synchronize()
+        ran4 = {e["name"] for e in L.usp_trace_collect()}
+    finally:
+        L.usp_trace_enable(False)
+    assert ran3.get("attn_block_order") == 3 and "attn_block_order" not in ran4, (ran3, ran4)
+    assert torch.equal(o3, o4) and torch.equal(l3, l4)
+    for a, b in zip(g3, g4):
+        assert torch.equal(a, b)
     # the forward's order, read back from its workspace (after the V copy:
     # costs, ranks, then the order), against the CPU replica of the costs
     from tests import kernel_geometry as G
