@@ -354,6 +354,21 @@ def test_bf16_document_block_order_only_schedules():
     cost = G.block_costs(m, 0, n, 64, 64)
     np.testing.assert_array_equal(tab[:n], cost)
     np.testing.assert_array_equal(tab[2 * part // 4:2 * part // 4 + n], G.longest_first(cost))
+    # the backward's two orders, after its required part (D and LSE*log2(e)
+    # rows; no row-chunk partials here): dK/dV key blocks of 128 keys over
+    # 64-row tiles, then dQ query blocks of 32 rows over 32-key tiles
+    bw = torch.empty(L.usp_attn_bwd_workspace_bytes(s, hq, hkv, d, L.USP_BF16), dtype=torch.uint8,
+                     device=dev)
+    L.usp_attn_bwd(q, k, v, o1, l1, do, cu_seqlens=cu, workspace=bw)
+    torch.cuda.synchronize()
+    req = 2 * (-(-hq * ((s + 127) // 128 * 128) * 4 // 256) * 256)
+    for kind, nb, block, tile in ((1, -(-s // 128), 128, 64), (0, -(-s // 32), 32, 32)):
+        part = -(-nb * 4 // 256) * 256
+        tab = bw[req:req + 3 * part].cpu().view(torch.int32).numpy()
+        cost = G.block_costs(m, kind, nb, block, tile)
+        np.testing.assert_array_equal(tab[:nb], cost)
+        np.testing.assert_array_equal(tab[2 * part // 4:2 * part // 4 + nb], G.longest_first(cost))
+        req += 3 * part
 
 
 def key_fixture(name):
