@@ -32,7 +32,8 @@
 //   * Preprocess: D = rowsum(dO * O) and LSE * log2(e).
 //   * Tiles go straight from global memory into double-buffered, swizzled LDS
 //     slots; masks are applied only on boundary tiles, and the causal
-//     triangle is launched heaviest-first.
+//     triangle is launched heaviest-first (with packed documents, in a
+//     longest-first order computed on the device, as in the forward).
 //   * Short sequences, where either grid would leave compute units idle and
 //     the causal triangle's longest blocks would set the time: the dK/dV
 //     kernel splits each key block's rows into chunks, and the dQ kernel

@@ -52,7 +52,10 @@
 //   * Causal / document / padding masks are applied only on tiles that cross
 //     a boundary; tiles entirely outside every row's range are never visited.
 //   * Workgroups are launched heaviest-first (last query block first) so the
-//     causal triangle's long rows start early and the tail is short.
+//     causal triangle's long rows start early and the tail is short. With
+//     packed documents that order interleaves long and short blocks, so a
+//     one-pass call takes a longest-first order computed on the device from
+//     the documents (splits.hip), which changes only the schedule.
 //   * Short sequences (a grid of a few hundred workgroups) split each query
 //     block's key tiles into consecutive pieces run by separate workgroups
 //     (planned in splits.hip); each writes an fp32 partial O and its LSE, and
