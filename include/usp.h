@@ -203,7 +203,8 @@ int usp_attn_bwd(const void* q, const void* k, const void* v, const void* o,
  *     before any device work: for example 120,000 rows with 4 query heads
  *     need 3.8 MB and 131,072 rows with 16 heads 16.8 MB, but 8,192 rows on
  *     one KV head (16 row chunks, 134 MB) are rejected. Room left in the array
- *     goes to dQ key splits as in usp_attn_bwd.
+ *     goes to dQ key splits, or to the longest-first block order of calls
+ *     with cu_seqlens, as in usp_attn_bwd.
  */
 int usp_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
