@@ -21,9 +21,11 @@ def seeded(shape, seed):
 
 CALLS = [
     # S, s_valid, hq, hkv, cu_seqlens; in this order, each smaller than the last
-    (16384, 16384, 32, 8, None),                 # one dK/dV row chunk, no dQ key splits
+    (16384, 16384, 32, 8, [0, 5000, 5001, 12000, 16384]),  # one row chunk, no dQ key
+                                                 # splits, longest-first block order
+    (16320, 16320, 32, 8, None),                 # one row chunk, no dQ key splits
     (1000, 997, 4, 1, None),                     # 16 row chunks, dQ key splits, padding
-    (777, 777, 8, 2, [0, 300, 301, 777]),        # 13 row chunks, documents
+    (777, 777, 8, 2, [0, 300, 301, 777]),        # 2 row chunks, documents
 ]
 
 
@@ -50,9 +52,18 @@ def test_noalloc_backward_matches_usp_attn_bwd_on_successive_calls():
         # outputs preallocated and filled with garbage: the call must overwrite them
         got = tuple(torch.full_like(t, float("nan")) for t in ref)
         cu_dev = None if cu is None else torch.tensor(cu, dtype=torch.int32, device=dev)
-        L.usp_attn_bwd_noalloc(qd, kd, vd, o, lse, dod, s_valid=s_valid, cu_seqlens=cu_dev,
-                               dq=got[0], dk=got[1], dv=got[2])
-        torch.cuda.synchronize()
+        L.usp_trace_collect()
+        L.usp_trace_enable(True)
+        try:
+            L.usp_attn_bwd_noalloc(qd, kd, vd, o, lse, dod, s_valid=s_valid, cu_seqlens=cu_dev,
+                                   dq=got[0], dk=got[1], dv=got[2])
+            torch.cuda.synchronize()
+            ran = {e["name"]: e["launches"] for e in L.usp_trace_collect()}
+        finally:
+            L.usp_trace_enable(False)
+        # the order tables of the dK/dV and dQ grids live in the static array too
+        if n == 0:
+            assert ran.get("attn_block_order") == 2, ran
         say(f"  required workspace {need} bytes")
         for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"call {n} {name} differs"
