@@ -348,6 +348,13 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
   // a compile-time constant, and instantiated per role so that each wave runs
   // straight-line code for its own role (with the role as a run-time branch
   // this compiler joined P, dS and the accumulators with register copies)
+  // Role 1's dP accumulators live across tiles. Every active tile starts
+  // them from zero, and an inactive tile reads nothing, so the results are
+  // unchanged. With per-tile accumulators this compiler filled them with
+  // zeros ahead of each tile's branch (32 moves per tile).
+  f32x16 pa1[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) pa1[mb] = f32x16{};
   auto tile = [&](int it, auto parity, auto role_c) __attribute__((always_inline)) {
     constexpr int buf = decltype(parity)::value;  // == it & 1
     constexpr int R = decltype(role_c)::value;    // == role
@@ -361,7 +368,8 @@ __global__ __launch_bounds__(128 * KG, (KG == 2 ? 2 : 1)) void bwd_dkdv_kernel(B
     const bool active = wave_live && r0 + BQ - 1 >= wr_lo && r0 <= wr_hi;
 
     // phase 1: role 0 -> P (to LDS and registers); role 1 -> dP (registers)
-    f32x16 pa[MB];
+    f32x16 pa0[MB];
+    f32x16 (&pa)[MB] = R == 1 ? pa1 : pa0;
     bf16x8 pb[NCH];
     if (active) {
 #pragma unroll
