@@ -62,6 +62,11 @@ SMALL = [
     ("tiny_bidir_33", 33, 30, 4, 2, None, False),
     # 8 query heads per KV head: two head chunks per KV head
     ("gqa8", 300, 300, 8, 1, None, True),
+    # 3 query heads per KV head: one head per workgroup (256 rows), three head
+    # chunks per KV head
+    ("gqa3_6q2kv", 700, 700, 6, 2, None, True),
+    # 16 query heads per KV head: four head chunks per KV head, padded keys
+    ("gqa16_padded", 600, 590, 16, 1, None, True),
     # head dim 64 (128-byte rows: their own tile swizzle and load mapping)
     ("d64_ragged", 300, 300, 4, 1, None, True, 64),
     ("d64_padded_gqa2", 1000, 997, 4, 2, None, True, 64),
