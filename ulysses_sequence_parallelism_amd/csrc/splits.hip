@@ -153,8 +153,17 @@ __global__ __launch_bounds__(256) void block_scatter_kernel(const int* __restric
 
 size_t block_order_bytes(int64_t n) { return (size_t)((n * 4 + 255) / 256 * 256) * 3; }
 
+constexpr int kMaxOrderBlocks = 131072;
+
 int block_order_launch(const MaskGeom& m, int kind, int n, int block, int tile, void* room,
                        hipStream_t stream, const int** order) {
+  // The rank kernel's work grows with n^2 and its grid is (n/256)^2
+  // workgroups: past 131,072 blocks (8.4M rows at 64 per block) the call keeps
+  // the natural order, which gives the same results.
+  if (n < 1 || n > kMaxOrderBlocks) {
+    *order = nullptr;
+    return USP_OK;
+  }
   const size_t part = block_order_bytes(n) / 3;
   int* cost = static_cast<int*>(room);
   int* rank = reinterpret_cast<int*>(static_cast<char*>(room) + part);

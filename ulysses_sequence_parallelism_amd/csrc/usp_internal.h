@@ -128,7 +128,8 @@ SplitPlan plan_key_splits(const SplitProblem& p);
 // (splits.hip): kind kOrderQueryBlocks (blocks of `block` query rows over key
 // tiles of `tile`) or kOrderKeyBlocks (blocks of `block` keys over row tiles of
 // `tile`). Needs block_order_bytes(n) bytes of device memory at `room`; on
-// success *order points into it (n block indexes, longest first).
+// success *order points into it (n block indexes, longest first), or is NULL
+// (the natural order) for more than 131,072 blocks.
 enum { kOrderQueryBlocks = 0, kOrderKeyBlocks = 1 };
 size_t block_order_bytes(int64_t n);
 int block_order_launch(const MaskGeom& m, int kind, int n, int block, int tile, void* room,
