@@ -11,11 +11,11 @@
 //   * the flat index t walks the token-major tensor X in order, so every
 //     access to X is perfectly coalesced and every run of Y (hp*d elements,
 //     256 B .. 4 KiB here) is written or read contiguously;
-//   * 16-byte chunks per lane. The unpack keeps 4 independent chunks in
+//   * 16-byte chunks per lane. The unpack keeps 3 independent chunks in
 //     flight per lane (all loads issued before the stores) to cover HBM
 //     latency; the pack, whose stores scatter into P runs, runs one chunk per
-//     lane in four times as many workgroups (measured: 6.38 against
-//     5.90 TB/s; the unpack is fastest with 4);
+//     lane in more workgroups (measured: 6.38 TB/s against 5.90 with 4; the
+//     unpack measured best at 3 of 2, 3, 4, 6, 8);
 //   * non-temporal loads and stores: nothing is reused, so the copy streams
 //     past the caches instead of evicting the attention working set;
 //   * integer division by the run and row lengths uses a multiply-high
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void permute_kernel(const Chunk* __restrict__ 
 template <typename Chunk, bool kPack>
 int launch(const void* src, void* dst, int64_t s_real, int64_t s_pad, int64_t row_bytes,
            int64_t run_bytes, hipStream_t stream) {
-  constexpr int kUnroll = kPack ? 1 : 4;
+  constexpr int kUnroll = kPack ? 1 : 3;
   const int64_t rows = kPack ? s_pad : s_real;
   const int64_t row_chunks = row_bytes / (int64_t)sizeof(Chunk);
   const int64_t run_chunks = run_bytes / (int64_t)sizeof(Chunk);
