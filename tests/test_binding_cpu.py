@@ -1,7 +1,8 @@
 """CPU-side checks of the Python binding: every tensor it hands to the C ABI
-must have the shape and dtype the call assumes (the library sees only
-pointers), and packed-document offsets are validated on the host. All of
-these raise before any device call, so they run without a GPU."""
+must have the shape and dtype the call assumes and be a GPU tensor (the
+library sees only device pointers), and packed-document offsets are validated
+on the host. All of these raise before any device call, so they run without a
+GPU."""
 import os
 
 import pytest
@@ -105,3 +106,27 @@ def test_interval_document_offsets_must_cover_the_call():
         usp.usp_attn_fwd_interval(q, k, v, q_off=110, k_off=50, cu_seqlens=[0, 70, 149])
     with pytest.raises(usp.UspError):
         usp.usp_attn_fwd_interval(q, k, v, q_off=0, k_off=0, cu_seqlens=[0, 50, 40, 150])
+
+
+def test_host_tensors_are_refused_before_the_call():
+    """Correct shapes and dtypes, but host tensors: a host pointer must never
+    reach a kernel."""
+    q, k, v = bf(64, 4, 128), bf(64, 1, 128), bf(64, 1, 128)
+    o, do, lse = bf(64, 4, 128), bf(64, 4, 128), f32(4, 64)
+    gpu = "must be on a GPU"
+    with pytest.raises(ValueError, match=gpu):
+        usp.usp_attn_fwd(q, k, v)
+    with pytest.raises(ValueError, match=gpu):
+        usp.usp_attn_bwd(q, k, v, o, lse, do)
+    with pytest.raises(ValueError, match=gpu):
+        usp.usp_attn_bwd_noalloc(q, k, v, o, lse, do)
+    with pytest.raises(ValueError, match=gpu):
+        usp.usp_attn_fwd_interval(q, k, v)
+    with pytest.raises(ValueError, match=gpu):
+        usp.usp_attn_bwd_interval(q, k, v, o, lse, do)
+    with pytest.raises(ValueError, match=gpu):
+        usp.usp_attn_merge(f32(64, 4, 128), lse, f32(64, 4, 128), lse)
+    with pytest.raises(ValueError, match=gpu):
+        usp.usp_pad_pack_seq2head(bf(10, 8, 64), 4)
+    with pytest.raises(ValueError, match=gpu):
+        usp.usp_unpack_head2seq(bf(4, 12, 2, 64), 10)

@@ -447,3 +447,21 @@ def test_workload(name):
         assert err <= 1e-3 * np.abs(dv64[a:b]).sum(axis=0).max() + 1e-3, (a, b, err)
     if w.s < w.s_pad:
         assert (dk64[w.s:] == 0).all() and (dv64[w.s:] == 0).all()
+
+
+def test_a_single_host_tensor_is_refused():
+    """GPU inputs with one host tensor among the outputs or the workspace: the
+    binding refuses the call before the library sees a host pointer."""
+    import ulysses_sequence_parallelism_amd as L
+    dev = gpu()
+    q = torch.zeros((128, 4, 128), dtype=torch.bfloat16, device=dev)
+    k = torch.zeros((128, 1, 128), dtype=torch.bfloat16, device=dev)
+    v = torch.zeros_like(k)
+    with pytest.raises(ValueError, match="must be on a GPU"):
+        L.usp_attn_fwd(q, k, v, out=torch.zeros((128, 4, 128), dtype=torch.bfloat16))
+    ws = torch.empty(L.usp_attn_fwd_workspace_bytes(128, 4, 1, 128, L.USP_BF16), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="must be on a GPU"):
+        L.usp_attn_fwd(q, k, v, workspace=ws)
+    o, lse = L.usp_attn_fwd(q, k, v)  # the same call on the GPU goes through
+    torch.cuda.synchronize()
+    assert o.is_cuda and lse.is_cuda

@@ -123,10 +123,35 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream=None):
+def _stream(stream=None, dev=None):
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(dev)
+    elif dev is not None and stream.device != dev:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {dev}")
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _on_gpu(fn, *ts):
+    """The device of the call. Every tensor handed to the C ABI must be a GPU
+    tensor, all on one device: the library takes raw device pointers, and a host
+    pointer would reach a kernel."""
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{fn}: every tensor must be on a GPU (got one on {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{fn}: tensors on {dev} and {t.device}; all must be on one GPU")
+    return dev
+
+
+def _call(fn, dev, stream, cfun, *args):
+    """Call cfun(*args, stream) with dev as the current device."""
+    with torch.cuda.device(dev):
+        _check(fn, cfun(*args, _stream(stream, dev)))
 
 
 def _check(fn: str, status: int):
@@ -186,9 +211,9 @@ def usp_pad_pack_seq2head(x: torch.Tensor, p: int, out: torch.Tensor | None = No
     if p >= 1 and h % p == 0:
         _shapes("usp_pad_pack_seq2head", out=(out, (p, s_pad, h // p, d)))
     _same_dtype("usp_pad_pack_seq2head", x.dtype, out=out)
-    _check("usp_pad_pack_seq2head",
-           lib().usp_pad_pack_seq2head(_ptr(x), _ptr(out), s_real, p, h, d, _dtype(x),
-                                       _stream(stream)))
+    dev = _on_gpu("usp_pad_pack_seq2head", x, out)
+    _call("usp_pad_pack_seq2head", dev, stream, lib().usp_pad_pack_seq2head,
+          _ptr(x), _ptr(out), s_real, p, h, d, _dtype(x))
     return out
 
 
@@ -204,9 +229,9 @@ def usp_unpack_head2seq(y: torch.Tensor, s_real: int, out: torch.Tensor | None =
     _contig(out)
     _shapes("usp_unpack_head2seq", out=(out, (s_real, p * hp, d)))
     _same_dtype("usp_unpack_head2seq", y.dtype, out=out)
-    _check("usp_unpack_head2seq",
-           lib().usp_unpack_head2seq(_ptr(y), _ptr(out), s_real, p, p * hp, d, _dtype(y),
-                                     _stream(stream)))
+    dev = _on_gpu("usp_unpack_head2seq", y, out)
+    _call("usp_unpack_head2seq", dev, stream, lib().usp_unpack_head2seq,
+          _ptr(y), _ptr(out), s_real, p, p * hp, d, _dtype(y))
     return out
 
 
@@ -289,10 +314,11 @@ def usp_attn_fwd(q, k, v, s_valid=None, cu_seqlens=None, causal=True, softmax_sc
     _same_dtype("usp_attn_fwd", q.dtype, k=k, v=v, out=out)
     _same_dtype("usp_attn_fwd", torch.float32, lse=lse)
     ws = _workspace(usp_attn_fwd_workspace_bytes(s_pad, hq, hkv, d, dt), q.device, workspace)
-    _check("usp_attn_fwd", lib().usp_attn_fwd(
+    dev = _on_gpu("usp_attn_fwd", q, k, v, out, lse, ws, cu)
+    _call("usp_attn_fwd", dev, stream, lib().usp_attn_fwd,
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), s_pad, s_valid, _ptr(cu), n_docs,
-        hq, hkv, d, scale, int(causal), dt, _stream(stream)))
+        hq, hkv, d, scale, int(causal), dt)
     return out, lse
 
 
@@ -316,10 +342,11 @@ def usp_attn_bwd(q, k, v, o, lse, dout, s_valid=None, cu_seqlens=None, causal=Tr
     _same_dtype("usp_attn_bwd", q.dtype, k=k, v=v, o=o, dout=dout, dq=dq, dk=dk, dv=dv)
     _same_dtype("usp_attn_bwd", torch.float32, lse=lse)
     ws = _workspace(usp_attn_bwd_workspace_bytes(s_pad, hq, hkv, d, dt), q.device, workspace)
-    _check("usp_attn_bwd", lib().usp_attn_bwd(
+    dev = _on_gpu("usp_attn_bwd", q, k, v, o, lse, dout, dq, dk, dv, ws, cu)
+    _call("usp_attn_bwd", dev, stream, lib().usp_attn_bwd,
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), s_pad, s_valid, _ptr(cu),
-        n_docs, hq, hkv, d, scale, int(causal), dt, _stream(stream)))
+        n_docs, hq, hkv, d, scale, int(causal), dt)
     return dq, dk, dv
 
 
@@ -351,9 +378,10 @@ def usp_attn_bwd_noalloc(q, k, v, o, lse, dout, s_valid=None, cu_seqlens=None, c
             dv=(dv, kshape))
     _same_dtype("usp_attn_bwd_noalloc", q.dtype, k=k, v=v, o=o, dout=dout, dq=dq, dk=dk, dv=dv)
     _same_dtype("usp_attn_bwd_noalloc", torch.float32, lse=lse)
-    _check("usp_attn_bwd_noalloc", lib().usp_attn_bwd_noalloc(
+    dev = _on_gpu("usp_attn_bwd_noalloc", q, k, v, o, lse, dout, dq, dk, dv, cu)
+    _call("usp_attn_bwd_noalloc", dev, stream, lib().usp_attn_bwd_noalloc,
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-        s_pad, s_valid, _ptr(cu), n_docs, hq, hkv, d, scale, int(causal), dt, _stream(stream)))
+        s_pad, s_valid, _ptr(cu), n_docs, hq, hkv, d, scale, int(causal), dt)
     return dq, dk, dv
 
 
@@ -408,10 +436,11 @@ def usp_attn_fwd_interval(q, k, v, q_off=0, k_off=0, s_k_valid=None, cu_seqlens=
     _same_dtype("usp_attn_fwd_interval", q.dtype, k=k, v=v)
     _same_dtype("usp_attn_fwd_interval", torch.float32, lse=lse)
     ws = _workspace(usp_attn_fwd_workspace_bytes(s_k, hq, hkv, d, dt), q.device, workspace)
-    _check("usp_attn_fwd_interval", lib().usp_attn_fwd_interval(
+    dev = _on_gpu("usp_attn_fwd_interval", q, k, v, out, lse, ws, cu)
+    _call("usp_attn_fwd_interval", dev, stream, lib().usp_attn_fwd_interval,
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), s_q, q_off, s_k, k_off, s_k_valid,
-        _ptr(cu), n_docs, hq, hkv, d, scale, int(causal), dt, _dtype(out), _stream(stream)))
+        _ptr(cu), n_docs, hq, hkv, d, scale, int(causal), dt, _dtype(out))
     return out, lse
 
 
@@ -431,9 +460,10 @@ def usp_attn_merge(o_a, lse_a, o_b, lse_b, out=None, lse=None, out_dtype=torch.f
             lse_b=(lse_b, (hq, s_q)), out=(out, o_a.shape), lse=(lse, (hq, s_q)))
     _same_dtype("usp_attn_merge", torch.float32, o_a=o_a, o_b=o_b, lse_a=lse_a, lse_b=lse_b,
                 lse=lse)
-    _check("usp_attn_merge", lib().usp_attn_merge(
+    dev = _on_gpu("usp_attn_merge", o_a, lse_a, o_b, lse_b, out, lse)
+    _call("usp_attn_merge", dev, stream, lib().usp_attn_merge,
         _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(out), _ptr(lse), s_q, hq, d,
-        _dtype(out), _stream(stream)))
+        _dtype(out))
     return out, lse
 
 
@@ -471,9 +501,9 @@ def usp_attn_bwd_interval(q, k, v, o, lse, dout, q_off=0, k_off=0, s_k_valid=Non
         raise UspError("usp_attn_bwd_interval", -1)
     ws = _workspace(usp_attn_bwd_interval_workspace_bytes(s_q, s_k, hq, hkv, d, dt), q.device,
                     workspace)
-    _check("usp_attn_bwd_interval", lib().usp_attn_bwd_interval(
+    dev = _on_gpu("usp_attn_bwd_interval", q, k, v, o, lse, dout, dq, dk, dv, ws, cu)
+    _call("usp_attn_bwd_interval", dev, stream, lib().usp_attn_bwd_interval,
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), s_q, q_off, s_k, k_off,
-        s_k_valid, _ptr(cu), n_docs, hq, hkv, d, scale, int(causal), dt, gdt, int(accumulate),
-        _stream(stream)))
+        s_k_valid, _ptr(cu), n_docs, hq, hkv, d, scale, int(causal), dt, gdt, int(accumulate))
     return dq, dk, dv
