@@ -17,12 +17,15 @@
  * sequences).
  *
  * Conventions for every call:
- *   - All tensor pointers are DEVICE memory owned by the caller; the library
- *     never allocates device memory and keeps no state between calls (apart
- *     from the optional kernel trace below and the static workspace array of
- *     usp_attn_bwd_noalloc).
- *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
- *     void*; NULL means the default stream). The return value is known
+ *   - All tensor pointers are DEVICE memory of the current device, owned by
+ *     the caller; the library never allocates device memory and keeps no state
+ *     between calls (apart from the optional kernel trace below and the static
+ *     workspace array of usp_attn_bwd_noalloc). The library cannot tell a host
+ *     pointer or another device's pointer from a valid one: passing one is
+ *     undefined (the kernels would access it). The Python binding refuses such
+ *     tensors before the call.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t of the current
+ *     device passed as void*; NULL means the default stream). The return value is known
  *     synchronously: argument checks run on the host before any HIP call, so a
  *     rejected call enqueues nothing.
  *   - Tensor pointers must be 16-byte aligned; outputs may not overlap inputs.
