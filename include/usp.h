@@ -60,6 +60,24 @@ int usp_version(void);
 const char* usp_status_string(int status);
 
 /*
+ * Optional checks of the caller's buffers, for debugging. When on, every call
+ * first asks the HIP runtime about each tensor it is given (its byte range
+ * from the shapes): the range must lie inside one device or managed allocation
+ * of the current device, or the call returns USP_ERR_INVALID and enqueues
+ * nothing. Catches host pointers, another device's pointers and buffers
+ * smaller than their shape inside a plain hipMalloc allocation; inside a pool
+ * that sub-allocates (such as torch's caching allocator) the allocation is the
+ * pool's segment, so only ranges that leave the segment are caught. Off by
+ * default (two runtime queries per tensor); initially on when the environment
+ * variable USP_CHECK_BUFFERS is set to anything but "0" at the library's first
+ * use.
+ *   on: 1 turns the checks on, 0 off, a negative value leaves them as they are.
+ * Returns the previous state (1 on, 0 off). Thread-safe; affects calls that
+ * start after it returns.
+ */
+int usp_check_buffers(int on);
+
+/*
  * Padded sequence length for a Ulysses degree p: the smallest multiple of p
  * that is >= s_real (alignment padding before sharding, "feat(dspark)",
  * Modifications). Returns -1 if p < 1 or s_real < 0.

@@ -51,10 +51,24 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.usp_version() == 120
+    assert L.usp_version() == 121
     for s in (OK, INVALID, UNSUPPORTED, NULLP, HIPERR, WORKSPACE, 12345):
         assert isinstance(L.usp_status_string(s), bytes)
     assert L.usp_status_string(0) == b"ok"
+
+
+def test_buffer_checks_toggle(L):
+    """usp_check_buffers sets the optional buffer checks and returns the
+    previous state; a negative argument only reads it."""
+    start = L.usp_check_buffers(-1)
+    assert start in (0, 1)
+    try:
+        assert L.usp_check_buffers(1) == start
+        assert L.usp_check_buffers(-1) == 1
+        assert L.usp_check_buffers(0) == 1
+        assert L.usp_check_buffers(-1) == 0
+    finally:
+        L.usp_check_buffers(start)
 
 
 def test_padded_len_matches_oracle(L):

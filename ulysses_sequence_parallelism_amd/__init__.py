@@ -21,6 +21,7 @@ __all__ = [
     "UspError",
     "lib",
     "usp_version",
+    "usp_check_buffers",
     "usp_status_string",
     "usp_padded_len",
     "usp_pad_pack_seq2head",
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
                                  ctypes.c_float, ctypes.c_size_t)
         L.usp_version.restype = i32
         L.usp_version.argtypes = []
+        L.usp_check_buffers.restype = i32
+        L.usp_check_buffers.argtypes = [i32]
         L.usp_status_string.restype = ctypes.c_char_p
         L.usp_status_string.argtypes = [i32]
         L.usp_padded_len.restype = i64
@@ -167,6 +170,12 @@ def _dtype(t: torch.Tensor) -> int:
 
 def usp_version() -> int:
     return lib().usp_version()
+
+
+def usp_check_buffers(on: bool | None = None) -> bool:
+    """Turn the library's optional buffer checks on or off (None: leave them);
+    returns the previous state (see usp.h)."""
+    return bool(lib().usp_check_buffers(-1 if on is None else int(bool(on))))
 
 
 def usp_status_string(status: int) -> str:

@@ -1,9 +1,13 @@
 // C ABI entry points of libusp: host-side argument checks, then kernel
 // dispatch. Every check runs before the first HIP call, so a rejected call
 // enqueues nothing and touches no device state (and can be exercised on a
-// machine without a GPU).
+// machine without a GPU). The optional buffer checks (usp_check_buffers) are
+// the exception: they query the HIP runtime about the caller's pointers, still
+// before anything is enqueued.
 #include <math.h>
+#include <stdlib.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "usp_common.h"
@@ -11,7 +15,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 120;
+constexpr int kAbiVersion = 121;
 
 size_t elem_bytes(int dtype) { return dtype == USP_BF16 ? 2 : 4; }
 
@@ -26,6 +30,64 @@ bool overlap(Span a, Span b) {
   if (a.p == nullptr || b.p == nullptr || a.n == 0 || b.n == 0) return false;
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
   return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// Optional checks of the caller's buffers (usp_check_buffers; initially on
+// when USP_CHECK_BUFFERS is set to a value other than 0 when the library is
+// first used): every span must lie inside one device (or managed) allocation
+// of the current device. Off by default: each span costs two runtime queries.
+// Inside a sub-allocating pool (torch's caching allocator) the allocation is
+// the pool's segment, so an undersized tensor inside a segment is not caught;
+// host pointers and other devices' pointers are.
+std::atomic<int> g_check_buffers{-1};  // -1: the environment not read yet
+
+bool check_buffers_on() {
+  int v = g_check_buffers.load();
+  if (v < 0) {
+    const char* e = getenv("USP_CHECK_BUFFERS");
+    const int want = (e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0')) ? 1 : 0;
+    g_check_buffers.compare_exchange_strong(v, want);
+    v = g_check_buffers.load();
+  }
+  return v == 1;
+}
+
+int check_buffer(const Span& s, int dev) {
+  if (s.p == nullptr || s.n == 0) return USP_OK;
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, s.p) != hipSuccess) {
+    (void)hipGetLastError();  // a failed query is not a launch error
+    return USP_ERR_INVALID;
+  }
+  if ((at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeManaged) || at.device != dev)
+    return USP_ERR_INVALID;
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void*>(s.p)) != hipSuccess) {
+    (void)hipGetLastError();
+    return USP_ERR_INVALID;
+  }
+  const uintptr_t b = reinterpret_cast<uintptr_t>(base), p = reinterpret_cast<uintptr_t>(s.p);
+  return (p >= b && p - b <= size && s.n <= size - (p - b)) ? USP_OK : USP_ERR_INVALID;
+}
+
+// Checks the n spans at s (when the checks are on).
+int check_buffers(const Span* s, int n) {
+  if (!check_buffers_on()) return USP_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return USP_ERR_HIP;
+  }
+  for (int i = 0; i < n; ++i) {
+    const int rc = check_buffer(s[i], dev);
+    if (rc != USP_OK) return rc;
+  }
+  return USP_OK;
+}
+
+Span cu_span(const int32_t* cu, int n_docs) {
+  return {cu, cu != nullptr && n_docs > 0 ? (size_t)(n_docs + 1) * 4 : 0};
 }
 
 int check_permute(const void* src, const void* dst, int64_t s_real, int p, int h, int d,
@@ -111,10 +173,15 @@ int fwd_checked(const void* q, const void* k, const void* v, void* o, float* lse
   // bf16: the key-major V copy is required; room beyond it (as much as
   // usp_attn_fwd_workspace_bytes) lets a short call split its keys
   const size_t need = dtype == USP_BF16 ? usp::attn_fwd_bf16_min_workspace(s_k, hkv, d) : 0;
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return USP_ERR_WORKSPACE;
-  if (need > 0 && !aligned16(workspace)) return USP_ERR_INVALID;
   const Span ins[] = {{q, qb}, {k, kb}, {v, kb}};
   const Span outs[] = {{o, ob}, {lse, lb}, {workspace, need > 0 ? workspace_bytes : 0}};
+  // the optional buffer checks come before the workspace size check, so a
+  // call with an undersized workspace exercises them without launching
+  const Span all[] = {ins[0], ins[1], ins[2], outs[0], outs[1], outs[2], cu_span(cu, n_docs)};
+  const int rc = check_buffers(all, 7);
+  if (rc != USP_OK) return rc;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return USP_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return USP_ERR_INVALID;
   for (const Span& a : outs) {
     for (const Span& b : ins)
       if (overlap(a, b)) return USP_ERR_INVALID;
@@ -200,6 +267,10 @@ int bwd_checked(const void* q, const void* k, const void* v, const void* o, cons
     if (overlap(ws, b)) return USP_ERR_INVALID;
   for (const Span& b : sp.outs)
     if (overlap(ws, b)) return USP_ERR_INVALID;
+  const Span all[] = {sp.ins[0], sp.ins[1],  sp.ins[2],  sp.ins[3], sp.ins[4],
+                      sp.ins[5], sp.outs[0], sp.outs[1], sp.outs[2], ws, cu_span(cu, n_docs)};
+  rc = check_buffers(all, 11);
+  if (rc != USP_OK) return rc;
   return bwd_dispatch(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, s_q, q_off,
                       s_k, k_off, s_k_valid, cu, n_docs, hq, hkv, d, scale, causal, dtype,
                       grad_dtype, accumulate, stream);
@@ -237,6 +308,12 @@ extern "C" {
 
 int usp_version(void) { return kAbiVersion; }
 
+int usp_check_buffers(int on) {
+  const int prev = check_buffers_on() ? 1 : 0;
+  if (on >= 0) g_check_buffers.store(on ? 1 : 0);
+  return prev;
+}
+
 const char* usp_status_string(int status) {
   switch (status) {
     case USP_OK: return "ok";
@@ -269,6 +346,9 @@ static int permute_entry(bool pack, const void* src, void* dst, int64_t s_real, 
   if ((in_bytes > 0 && src == nullptr) || dst == nullptr) return USP_ERR_NULL;
   if (!aligned16(src) || !aligned16(dst)) return USP_ERR_INVALID;
   if (overlap({src, in_bytes}, {dst, out_bytes})) return USP_ERR_INVALID;
+  const Span all[] = {{src, in_bytes}, {dst, out_bytes}};
+  rc = check_buffers(all, 2);
+  if (rc != USP_OK) return rc;
   const int64_t row_bytes = (int64_t)h * d * (int64_t)elem_bytes(dtype);
   return usp::permute_launch(pack, src, dst, s_real, s_pad, p, row_bytes,
                              static_cast<hipStream_t>(stream));
@@ -336,7 +416,11 @@ int usp_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void
                     dtype, 0, &need, &sp);
   if (rc != USP_OK) return rc;
   if (need > (size_t)USP_NOALLOC_SCRATCH_BYTES) return USP_ERR_WORKSPACE;
-  // the first HIP call: every argument check has passed
+  const Span all[] = {sp.ins[0], sp.ins[1],  sp.ins[2],  sp.ins[3],  sp.ins[4],
+                      sp.ins[5], sp.outs[0], sp.outs[1], sp.outs[2], cu_span(cu_seqlens, n_docs)};
+  rc = check_buffers(all, 10);
+  if (rc != USP_OK) return rc;
+  // the first HIP call of the dispatch: every argument check has passed
   void* ws = nullptr;
   rc = scratch_of_current_device(&ws);
   if (rc != USP_OK) return rc;
@@ -421,6 +505,9 @@ int usp_attn_merge(const float* o_a, const float* lse_a, const float* o_b, const
     if (!same && overlap({lse, lb}, b)) return USP_ERR_INVALID;
   }
   if (overlap({o, oob}, {lse, lb})) return USP_ERR_INVALID;
+  const Span all[] = {o_ins[0], o_ins[1], o_ins[2], o_ins[3], {o, oob}, {lse, lb}};
+  const int rc = check_buffers(all, 6);
+  if (rc != USP_OK) return rc;
   return usp::attn_merge_launch(o_a, lse_a, o_b, lse_b, o, lse, s_q, hq, d,
                                 o_dtype == USP_FP32, static_cast<hipStream_t>(stream));
 }
