@@ -292,6 +292,20 @@ def _cu(cu_seqlens, s_pad, device):
     return host.to(device=device, dtype=torch.int32), host.numel() - 1
 
 
+def _cu_any(cu_seqlens, s_pad, device):
+    """cu_seqlens as given: a device int32 tensor is passed as is (the caller
+    has validated it; the kernels clamp every offset to the sequence, so a bad
+    one cannot reach memory out of range). This is the form to use under graph
+    capture, where host validation would copy. Anything else is validated on
+    the host and copied to the device."""
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda:
+        if (cu_seqlens.dtype != torch.int32 or cu_seqlens.ndim != 1
+                or not cu_seqlens.is_contiguous() or cu_seqlens.numel() < 2):
+            raise UspError("cu_seqlens", -1)
+        return cu_seqlens, cu_seqlens.numel() - 1
+    return _cu(cu_seqlens, s_pad, device)
+
+
 def _workspace(nbytes, device, workspace):
     if nbytes == 0:
         return None
@@ -305,14 +319,16 @@ def usp_attn_fwd(q, k, v, s_valid=None, cu_seqlens=None, causal=True, softmax_sc
     """Attention forward over one rank's share (see usp.h).
 
     q [s_pad, hq, d], k and v [s_pad, hkv, d]. Returns (o, lse) with
-    o [s_pad, hq, d] in q's dtype and lse [hq, s_pad] fp32."""
+    o [s_pad, hq, d] in q's dtype and lse [hq, s_pad] fp32. cu_seqlens: a
+    list or host tensor (validated here), or a device int32 tensor taken as
+    is (the form for graph capture)."""
     _contig(q, k, v)
     s_pad, hq, d = q.shape
     hkv = k.shape[1]
     s_valid = s_pad if s_valid is None else s_valid
     scale = float(d) ** -0.5 if softmax_scale is None else softmax_scale
     dt = _dtype(q)
-    cu, n_docs = _cu(cu_seqlens, s_pad, q.device)
+    cu, n_docs = _cu_any(cu_seqlens, s_pad, q.device)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -340,7 +356,7 @@ def usp_attn_bwd(q, k, v, o, lse, dout, s_valid=None, cu_seqlens=None, causal=Tr
     s_valid = s_pad if s_valid is None else s_valid
     scale = float(d) ** -0.5 if softmax_scale is None else softmax_scale
     dt = _dtype(q)
-    cu, n_docs = _cu(cu_seqlens, s_pad, q.device)
+    cu, n_docs = _cu_any(cu_seqlens, s_pad, q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -371,12 +387,7 @@ def usp_attn_bwd_noalloc(q, k, v, o, lse, dout, s_valid=None, cu_seqlens=None, c
     s_valid = s_pad if s_valid is None else s_valid
     scale = float(d) ** -0.5 if softmax_scale is None else softmax_scale
     dt = _dtype(q)
-    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda:
-        if cu_seqlens.dtype != torch.int32 or cu_seqlens.ndim != 1 or not cu_seqlens.is_contiguous():
-            raise UspError("cu_seqlens", -1)
-        cu, n_docs = cu_seqlens, cu_seqlens.numel() - 1
-    else:
-        cu, n_docs = _cu(cu_seqlens, s_pad, q.device)
+    cu, n_docs = _cu_any(cu_seqlens, s_pad, q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
