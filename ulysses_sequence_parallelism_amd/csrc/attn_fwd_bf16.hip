@@ -31,18 +31,20 @@
 //     O^T += V^T P^T (no LDS round trip); V is staged from a key-major copy
 //     whose 16-key chunks are reordered to match (see kmajor.hip).
 //   * Q stays in registers for the whole key loop (d / 16 x 16 bytes per lane).
-//   * K and V^T tiles of 64 keys are double-buffered in LDS and go straight
+//   * K and V^T tiles of 64 keys sit in three LDS slots each and go straight
 //     from global memory into LDS (global_load_lds_dwordx4: no staging
 //     registers, no LDS stores). That load writes each lane's 16 bytes at
 //     consecutive LDS addresses, so rows are unpadded and their 16-byte chunks
 //     XOR-swizzled (chunk c of a K row r in slot c ^ swz_row(r), of a 128-byte
 //     V^T row r in slot c ^ ((r >> 1) & 7)): 16 lanes reading one chunk of 16
-//     rows hit 16 distinct bank groups. The next tiles' loads are issued at
-//     the start of a step; one barrier per tile.
-//   * Software pipeline inside each wave: the scores of tile t+1 (MFMA) are
-//     computed in the same straight-line block as the softmax of tile t
-//     (VALU), so the two interleave; boundary tiles and running-max updates
-//     take a rarely used slow path.
+//     rows hit 16 distinct bank groups.
+//   * Ping-pong between the two waves of each SIMD: every tile has a softmax
+//     phase (row max, exponentials, row sums: vector work) and a matrix phase
+//     (the next tile's scores and this tile's P V: MFMA). The waves of one
+//     half of the workgroup run half a tile behind the other half, with a
+//     barrier between phases, so on every SIMD one wave feeds the matrix core
+//     while its partner does the vector work. Boundary tiles and running-max
+//     updates take a rarely used slow path inside the softmax phase.
 //   * Online softmax in the log2 domain (scale*log2(e) folded into one FMA
 //     before v_exp_f32) with a lazy, exact rescale: the running max is only
 //     raised when a row's tile max exceeds it by more than 8 (log2 units), so
@@ -104,10 +106,10 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
   constexpr int VPW = D / 8 / 8;     // V^T wave-loads (8 d-rows each) per wave and tile
   constexpr int QBW = 8 / HG;
   constexpr int QROWS = 32 * QBW;
-  // two slots per tensor in one array each, so that slot 1 sits exactly one
-  // tile after slot 0 (the fragment reads below add that as a constant)
-  __shared__ __attribute__((aligned(16))) __bf16 lk[2][BN * D];
-  __shared__ __attribute__((aligned(16))) __bf16 lv[2][D * BN];
+  // three slots per tensor in one array each, slot s sitting s tiles after
+  // slot 0 (the fragment reads below add that as a constant)
+  __shared__ __attribute__((aligned(16))) __bf16 lk[3][BN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 lv[3][D * BN];
   // filled only by direct loads, which this compiler does not count as stores
   asm volatile("" ::"s"(&lk[0][0]), "s"(&lv[0][0]) : "memory");
   auto kslot = [&](int b) -> __bf16* { return &lk[b][0]; };
@@ -177,12 +179,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
     return;
   }
 
-  // Software pipeline: the scores of tile t+1 are computed while tile t goes
-  // through the softmax, so one wave's MFMAs and vector work are independent
-  // and can interleave. K runs one tile ahead of V: at the start of step t,
-  // K(t+2) goes into K(t)'s slot and V(t+1) into V(t-1)'s (both last read in
-  // step t-1), so each needs two slots and there is one barrier per tile.
-  // A part is one 1 KiB wave-load: RPP keys of K or 8 d-rows of V^T. Wave w
+  // Tile loads. A part is one 1 KiB wave-load: RPP keys of K or 8 d-rows of V^T. Wave w
   // loads K parts KPW w .. +KPW-1 and V^T parts VPW w .. +VPW-1 as inline-asm
   // direct loads (lds_dma16): a wave-uniform base plus a 32-bit lane offset.
   const int wu = __builtin_amdgcn_readfirstlane(w);  // LDS destinations go to M0
@@ -249,7 +246,26 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
     }
   };
 
-  f32x16 sa[2], sb[2];
+  // Two wave groups take turns: while the waves of one group run a tile's
+  // matrix phase (the next tile's scores and this tile's P V, all MFMA), the
+  // waves of the other run a softmax phase (row max, mask and rescale when
+  // needed, exponentials, row sums: all vector work). Waves w and w + 4 share
+  // a SIMD, so each SIMD holds one wave of each group and its matrix core is
+  // fed by one while the other does the vector work. A barrier separates the
+  // phases; the second group runs half a tile behind the first.
+  // Tile t's K sits in K slot t % 3 and its V^T in V slot t % 3. The softmax
+  // phase of tile t loads K(t+2) into the slot of K(t-1), and the matrix phase
+  // of tile t loads V(t+1) into the slot of V(t-2); both were last read by the
+  // matrix phase of tile t-2, which both groups have finished by then. The
+  // other group's concurrent phase reads K(t+1) / V(t), K(t) / V(t-1) or no
+  // LDS at all, never a slot being written. The matrix phase waits for all of
+  // its wave's loads, so a tile's slots are complete at the barrier after both
+  // groups' matrix phases of the tile before. (Splitting the loads this way
+  // balances the two phases: all loads in the softmax phase, or all in the
+  // matrix phase, measured slower.)
+  const int grp = wu >> 2;
+  f32x16 sc[2];   // scores of the tile whose softmax phase comes next
+  bf16x8 pb[4];   // its probabilities, for the next matrix phase
   if (nt > 0) {
     load_k(0, 0);
     if (nt > 1) load_k(1, 1);
@@ -257,111 +273,121 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
   }
   wait_lds_dma();
   __syncthreads();
-  if (nt > 0) scores(0, sa);
-  __syncthreads();  // S(0) is read from slot 0 before iteration 0 refills it
+  if (nt > 0) scores(0, sc);
 
-  // one pipeline step; the score buffers and the slots swap roles every step,
-  // so the loop is unrolled instead of copying the next scores over the
-  // current
-  auto step = [&](int it, f32x16 (&scur)[2], f32x16 (&snext)[2], auto parity) {
-      const int t0 = tstart + it * BN;
-      constexpr int buf = decltype(parity)::value;  // == it & 1; K is read from slot buf ^ 1, V from buf
-      if (it + 2 < nt) load_k(it + 2, buf);
-      if (it + 1 < nt) load_v(it + 1, buf ^ 1);
-
-      // -- row max of this tile (both half-waves hold the row); a full tile
-      //    needs no mask
-      float mx = half_swap_max(max_of_32(scur[0], scur[1])) * pr.scale_log2;
-      const bool full = t0 >= free_lo && t0 + BN - 1 <= free_hi &&
-                        t0 >= wkmin && t0 + BN - 1 <= wkmax;
-      // -- slow path (boundary tiles and running-max updates, both rare): mask,
-      //    recompute the max, rescale O
-      if (__ballot(!full || mx > m_run + kRescaleThreshold)) {
-        if (!full) {
+  auto softmax = [&](int t) __attribute__((always_inline)) {
+    const int t0 = tstart + t * BN;
+    if (t + 2 < nt) load_k(t + 2, (t + 2) % 3);
+    // -- row max of this tile (both half-waves hold the row); a full tile
+    //    needs no mask
+    float mx = half_swap_max(max_of_32(sc[0], sc[1])) * pr.scale_log2;
+    const bool full = t0 >= free_lo && t0 + BN - 1 <= free_hi &&
+                      t0 >= wkmin && t0 + BN - 1 <= wkmax;
+    // -- slow path (boundary tiles and running-max updates, both rare): mask,
+    //    recompute the max, rescale O
+    if (__ballot(!full || mx > m_run + kRescaleThreshold)) {
+      if (!full) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = t0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-              if (key < lo || key > hi) scur[kb][i] = -INFINITY;
-            }
-          mx = half_swap_max(max_of_32(scur[0], scur[1])) * pr.scale_log2;
-        }
-        const bool need = mx > m_run + kRescaleThreshold;
-        if (__ballot(need)) {
-          const float mnew = need ? mx : m_run;
-          const float alpha = need ? exp2f(m_run - mnew) : 1.f;
-#pragma unroll
-          for (int b = 0; b < DB; ++b)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
-          l_run *= alpha;
-          m_run = mnew;
-        }
-      }
-      const float msub = m_run == -INFINITY ? 0.f : m_run;
-
-      // -- one straight-line block: the next tile's scores (MFMA; its slot holds
-      //    stale data on the last iteration and the result is then unused) and
-      //    this tile's probabilities (VALU) are independent and interleave
-      scores(buf ^ 1, snext);
-      bf16x8 pb[4];
-      float ls4[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          u32x4 pk;
-          float ls = 0.f;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][8 * c + 2 * t], pr.scale_log2, -msub));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][8 * c + 2 * t + 1], pr.scale_log2, -msub));
-            ls += p0 + p1;
-            pk[t] = pack_bf16x2(p0, p1);
+          for (int i = 0; i < 16; ++i) {
+            const int key = t0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+            if (key < lo || key > hi) sc[kb][i] = -INFINITY;
           }
-          ls4[kb * 2 + c] = ls;
-          pb[kb * 2 + c] = __builtin_bit_cast(bf16x8, pk);
+        mx = half_swap_max(max_of_32(sc[0], sc[1])) * pr.scale_log2;
+      }
+      const bool need = mx > m_run + kRescaleThreshold;
+      if (__ballot(need)) {
+        const float mnew = need ? mx : m_run;
+        const float alpha = need ? exp2f(m_run - mnew) : 1.f;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
+        l_run *= alpha;
+        m_run = mnew;
+      }
+    }
+    const float msub = m_run == -INFINITY ? 0.f : m_run;
+    float ls4[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        u32x4 pk;
+        float ls = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * c + 2 * u], pr.scale_log2, -msub));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * c + 2 * u + 1], pr.scale_log2, -msub));
+          ls += p0 + p1;
+          pk[u] = pack_bf16x2(p0, p1);
         }
+        ls4[kb * 2 + c] = ls;
+        pb[kb * 2 + c] = __builtin_bit_cast(bf16x8, pk);
       }
-      l_run += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
-
-      // -- O^T += V^T P^T
+    }
+    l_run += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
+    // P and the row sum are complete here: without this the compiler may
+    // sink the exponentials past the barrier into the matrix phase
 #pragma unroll
-      for (int ch = 0; ch < 4; ++ch) {
-#pragma unroll
-        for (int b = 0; b < DB; ++b) {
-          const bf16x8 vf = lds_read_b128(vra[ch] + (uint32_t)(buf * D * BN + b * 32 * BN) * 2);
-          oacc[b] = mfma32(vf, pb[ch], oacc[b]);
-        }
-      }
-      // Instruction order for this block: fragment reads run four ahead of
-      // the MFMAs that consume them (otherwise each MFMA waits on a read
-      // issued just before it), and the softmax work fills the score MFMAs'
-      // shadows.
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
-#pragma unroll
-      for (int i = 0; i < 2 * KK + 4 * DB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-      }
-
-      wait_lds_dma();  // this step's loads have landed
-      __syncthreads();
+    for (int i = 0; i < 4; ++i) {
+      u32x4 u = __builtin_bit_cast(u32x4, pb[i]);
+      asm volatile("" : "+v"(u));
+      pb[i] = __builtin_bit_cast(bf16x8, u);
+    }
+    asm volatile("" : "+v"(l_run));
   };
-  // Whole groups of four steps in the loop, the remainder after it. A loop
-  // with one exit keeps the softmax state in the same registers throughout;
-  // with an exit after every step this compiler needed about 20 more VGPRs.
+  // matrix phase of tile t: K(t+1) in slot KS = (t+1) % 3, V(t) in VS = t % 3.
+  // On the last tile K(t+1) does not exist and the scores are unused.
+  auto matrix = [&](int t, auto ks, auto vs) __attribute__((always_inline)) {
+    constexpr int KS = decltype(ks)::value, VS = decltype(vs)::value;
+    if (t + 1 < nt) load_v(t + 1, (t + 1) % 3);
+    scores(KS, sc);
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        const bf16x8 vf = lds_read_b128(vra[ch] + (uint32_t)(VS * D * BN + b * 32 * BN) * 2);
+        oacc[b] = mfma32(vf, pb[ch], oacc[b]);
+      }
+    }
+    // fragment reads run four ahead of the MFMAs that consume them
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
+#pragma unroll
+    for (int i = 0; i < 2 * KK + 4 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+    }
+    wait_lds_dma();  // this wave's loads of the last softmax phase have landed
+  };
+  // The phases must not leak into each other: without a scheduling fence the
+  // compiler moves register-only work (the exponentials) across a barrier.
+  auto phase_barrier = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Every wave runs softmax(t), barrier, matrix(t), barrier for each tile.
+  // The second group passes one barrier before its first tile and the first
+  // group one after its last, so both pass the same number of barriers and the
+  // second group's softmax phases meet the first group's matrix phases.
+  auto tile = [&](int t, auto ks, auto vs) __attribute__((always_inline)) {
+    softmax(t);
+    phase_barrier();
+    matrix(t, ks, vs);
+    phase_barrier();
+  };
+  if (grp == 1) phase_barrier();
   int it = 0;
-  for (; it + 4 <= nt; it += 4) {
-    step(it, sa, sb, std::integral_constant<int, 0>{});
-    step(it + 1, sb, sa, std::integral_constant<int, 1>{});
-    step(it + 2, sa, sb, std::integral_constant<int, 0>{});
-    step(it + 3, sb, sa, std::integral_constant<int, 1>{});
+  for (; it + 3 <= nt; it += 3) {
+    tile(it, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+    tile(it + 1, std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
+    tile(it + 2, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{});
   }
-  if (it < nt) step(it, sa, sb, std::integral_constant<int, 0>{});
-  if (it + 1 < nt) step(it + 1, sb, sa, std::integral_constant<int, 1>{});
-  if (it + 2 < nt) step(it + 2, sa, sb, std::integral_constant<int, 0>{});
+  if (it < nt) tile(it, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+  if (it + 1 < nt) tile(it + 1, std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
+  if (grp == 0) phase_barrier();
 
   const float l_tot = half_swap_sum(l_run);
   if (row_ok) {
