@@ -277,10 +277,11 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
 
   auto softmax = [&](int t) __attribute__((always_inline)) {
     const int t0 = tstart + t * BN;
-    if (t + 2 < nt) load_k(t + 2, (t + 2) % 3);
     // -- row max of this tile (both half-waves hold the row); a full tile
     //    needs no mask
     float mx = half_swap_max(max_of_32(sc[0], sc[1])) * pr.scale_log2;
+    // K(t+2) issued after the row max, not ahead of it (0.4% faster)
+    if (t + 2 < nt) load_k(t + 2, (t + 2) % 3);
     const bool full = t0 >= free_lo && t0 + BN - 1 <= free_hi &&
                       t0 >= wkmin && t0 + BN - 1 <= wkmax;
     // -- slow path (boundary tiles and running-max updates, both rare): mask,
