@@ -360,7 +360,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams pr) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
     }
-    wait_lds_dma();  // this wave's loads of the last softmax phase have landed
+    wait_lds_dma();  // this wave's K loads (softmax phase) and V loads (above) have landed
   };
   // The phases must not leak into each other: without a scheduling fence the
   // compiler moves register-only work (the exponentials) across a barrier.
