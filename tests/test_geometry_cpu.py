@@ -93,9 +93,10 @@ def check_bwd(L, m: G.Geom, hq, hkv, d, ws_bytes, what=""):
 
 
 def full_cases():
-    from tests.test_gpu_attention import LONG, SMALL
+    from tests.test_gpu_attention import LONG, SMALL, TILE_COUNTS
     from tests.test_gpu_key_splits import FULL
-    out = []
+    out = [(f"tiles_S{s}_{'causal' if c else 'bidir'}", s, s, 4, 1, None, c, 128)
+           for s, c, _ in TILE_COUNTS]
     for c in SMALL:
         name, s, s_valid, hq, hkv, cu, causal = c[:7]
         out.append((name, s, s_valid, hq, hkv, cu, causal, c[7] if len(c) > 7 else 128))

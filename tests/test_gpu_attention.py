@@ -465,3 +465,43 @@ def test_a_single_host_tensor_is_refused():
     o, lse = L.usp_attn_fwd(q, k, v)  # the same call on the GPU goes through
     torch.cuda.synchronize()
     assert o.is_cuda and lse.is_cuda
+
+
+# The forward runs two wave groups half a tile apart, with a barrier between
+# its softmax and matrix phases, a tile loop unrolled by three, and an extra
+# barrier for each group outside the loop. Every tile count modulo three, and
+# key splits that leave a workgroup few or no tiles, go through different
+# parts of that schedule.
+# Bidirectional S = 64 n gives every workgroup exactly n key tiles in one pass;
+# from about 1,000 rows the recommended workspace lets the call split (2 to 7
+# splits here), and causal splits of the early query blocks get no tiles.
+TILE_COUNTS = ([(64 * n, False, False) for n in range(1, 10)]
+               + [(64 * n + 17, True, False) for n in (1, 2, 3, 5)]
+               + [(1024, False, True), (1500, False, True), (3000, True, True), (4096, True, True)])
+
+
+@pytest.mark.parametrize("s,causal,splits_expected", TILE_COUNTS,
+                         ids=[f"S{s}_{'causal' if c else 'bidir'}" for s, c, _ in TILE_COUNTS])
+def test_bf16_forward_tile_counts_one_pass_and_split(s, causal, splits_expected):
+    L = usp()
+    dev = gpu()
+    hq, hkv, d = 4, 1, 128
+    q, k, v = (seeded((s, h, d), 3000 + s + i, torch.bfloat16) for i, h in enumerate((hq, hkv, hkv)))
+    q64, k64, v64 = (f64(t) for t in (q, k, v))
+    o_ref, lse_ref = oracle.attn_fwd(q64, k64, v64, d ** -0.5, s, None, causal)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    minimum = hkv * d * (-(-s // 128) * 128) * 2
+    full = L.usp_attn_fwd_workspace_bytes(s, hq, hkv, d, L.USP_BF16)
+    splits = []
+    for ws_bytes in (minimum, full):
+        z = L.usp_attn_fwd_num_splits(s, s, hq, hkv, d, L.USP_BF16, causal=causal,
+                                      workspace_bytes=ws_bytes)
+        splits.append(z)
+        say(f"S={s} causal={causal} workspace={ws_bytes} key splits={z}")
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        o, lse = L.usp_attn_fwd(qd, kd, vd, causal=causal, workspace=ws)
+        torch.cuda.synchronize()
+        check_close("O", f64(o), o_ref, "bf16")
+        check_close("LSE", f64(lse), lse_ref, "bf16")
+    assert splits[0] == 1
+    assert (splits[1] > 1) == splits_expected, splits
